@@ -1,0 +1,167 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused QK-RMSNorm + 3D M-RoPE joint text+image attention
+on one MI355X.
+
+One step = one full pass of the path over one batch: the prologue pass
+(rotary table + K') and the attention kernel, i.e. one ``mrope_attn_fwd``
+call, on inputs already resident in HBM. Default workload: the 1024px shape
+(B=1, H=32, head_dim=128, 512 text + 64x64 image tokens = 4608 tokens).
+
+Prints one JSON line. ``value`` is algorithmic TFLOP/s of the whole step
+(4*H*D*sum_b n_b^2 over real tokens), ``roofline`` the attention kernel's
+own rate (HIP events around that kernel on its stream) against the bf16
+dense MFMA peak, and ``cpu_baseline`` the fp64 oracle timed on the host on
+the same workload (with the GPU output checked against it).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused QK-norm+M-RoPE attention TFLOP/s & % bf16 MFMA peak, 4608 tok"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "diffusion_transformer_image_head_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(config: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"attn_bf16_{config}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, gpu_out):
+    """fp64 oracle on the host over the whole workload; also the parity check."""
+    import numpy as np
+    from oracle.reference import oracle_fwd
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    ref, _ = oracle_fwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens,
+                        text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps)
+    dt = time.perf_counter() - t0
+    d = gpu_out - ref
+    rel = float(np.sqrt((d * d).sum() / (ref * ref).sum()))
+    return {
+        "value": round(w.flops() / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle", "seconds": round(dt, 3),
+        "sample": f"the whole workload ({w.shape[2]} heads, all {w.shape[1]} query rows), fp64 NumPy",
+    }, {"max_abs": float(np.abs(d).max()), "rel_rms": rel}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="1024px", choices=["512px", "1024px", "ragged", "long"])
+    ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(heads/batch shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import lib, prepared_call
+    from diffusion_transformer_image_head_amd.workloads import config_workload
+
+    lib()  # fail loudly without the HIP library
+    dev = torch.device("cuda:0")
+    w = config_workload(args.config)
+    b, s, h, d = w.shape
+    q = torch.from_numpy(w.q).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(w.k).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(w.v).to(dev).to(torch.bfloat16)
+    pos = torch.from_numpy(w.pos).to(dev)
+    gq = torch.from_numpy(w.gamma_q).to(dev)
+    gk = torch.from_numpy(w.gamma_k).to(dev)
+    sl = None if w.seq_lens is None else torch.from_numpy(w.seq_lens).to(dev)
+    prepare, attend, out = prepared_call(q, k, v, pos, gq, gk, sl, text_pad=w.text_pad,
+                                         section=w.section, kprologue=args.kprologue)
+
+    for _ in range(args.warmup):
+        prepare()
+        attend()
+    torch.cuda.synchronize()
+
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        prepare()
+        mids[i].record()
+        attend()
+        ends[i].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    attn_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
+
+    flops = w.flops()
+    ms_step = total_ms / args.steps
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights)",
+        "config": {"workload": f"{args.config}: B={b} H={h} head_dim={d} tokens={s} "
+                               f"(text_pad={w.text_pad} + {w.grid[0]}x{w.grid[1]} image)",
+                   "batch": b, "heads": h, "head_dim": d, "seq_len": s,
+                   "section": list(w.section), "kprologue": args.kprologue,
+                   "text_lens": None if w.seq_lens is None else [int(x) for x in w.seq_lens]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(args.config),
+                     "kernel_ms": round(attn_ms, 5), "kernel": "attn_bf16_kernel"},
+        "frac_of_peak_whole_step": round(value / PEAK_BF16_TFLOPS, 4),
+        "wall_s": round(wall, 4),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        got = out.float().cpu().numpy().astype(np.float64)
+        base, parity = cpu_baseline(w, got)
+        rec["cpu_baseline"] = base
+        rec["parity"] = dict(parity, bars={"max_abs": 2e-2, "rel_rms": 5e-3},
+                             ok=bool(parity["max_abs"] <= 2e-2 and parity["rel_rms"] <= 5e-3))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""ctypes binding of libmrope_attn.so (argument marshalling only).
+
+Every step of the attention path runs in the HIP library. This module turns
+torch tensors into the C ABI's pointers, strides and stream, allocates the
+output / workspace through torch's caching allocator, and raises on a
+non-zero status. There is no fallback: without the built library, or for
+tensors not on a GPU, the call fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmrope_attn.so")
+
+MRA_BF16, MRA_FP32 = 0, 1
+KPRO_AUTO, KPRO_FUSED, KPRO_PREPASS = 0, 1, 2
+_KPRO = {"auto": KPRO_AUTO, "fused": KPRO_FUSED, "prepass": KPRO_PREPASS}
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``mra_desc`` (include/mrope_attn.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("text_pad", ctypes.c_int32),
+        ("section", ctypes.c_int32 * 3),
+        ("theta", ctypes.c_float), ("eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32), ("kprologue", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class MraError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"mrope_attn status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m diffusion_transformer_image_head_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        L.mrope_attn_validate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp]
+        L.mrope_attn_validate.restype = ctypes.c_int
+        L.mrope_attn_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        L.mrope_attn_workspace_size.restype = ctypes.c_size_t
+        L.mrope_attn_fwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp,
+                                     f32p, vp, ctypes.c_size_t, vp]
+        L.mrope_attn_fwd.restype = ctypes.c_int
+        L.mrope_attn_prepare.argtypes = [ctypes.POINTER(Desc), vp, i32p, f32p, vp, ctypes.c_size_t, vp]
+        L.mrope_attn_prepare.restype = ctypes.c_int
+        L.mrope_attn_attend.argtypes = L.mrope_attn_fwd.argtypes
+        L.mrope_attn_attend.restype = ctypes.c_int
+        L.mrope_attn_status_string.argtypes = [ctypes.c_int]
+        L.mrope_attn_status_string.restype = ctypes.c_char_p
+        L.mrope_attn_abi_version.argtypes = []
+        L.mrope_attn_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mrope_attn_status_string(status).decode()
+
+
+def make_desc(batch, seq, heads, head_dim, *, text_pad, section=(16, 24, 24), theta=10000.0,
+              eps=1e-6, scale=None, dtype=MRA_BF16, kprologue="auto",
+              q_stride=None, k_stride=None, v_stride=None, o_stride=None) -> Desc:
+    """Build a descriptor; strides default to contiguous [B, S, H, D]."""
+    d = Desc()
+    d.batch, d.seq, d.heads, d.head_dim, d.text_pad = batch, seq, heads, head_dim, text_pad
+    d.section[:] = [int(x) for x in section]
+    d.theta, d.eps = float(theta), float(eps)
+    d.softmax_scale = 0.0 if scale is None else float(scale)
+    d.dtype = dtype
+    d.kprologue = _KPRO[kprologue] if isinstance(kprologue, str) else int(kprologue)
+    cont = (seq * heads * head_dim, heads * head_dim, head_dim)
+    for name, st in (("q_stride", q_stride), ("k_stride", k_stride), ("v_stride", v_stride),
+                     ("o_stride", o_stride)):
+        getattr(d, name)[:] = list(cont if st is None else st)
+    return d
+
+
+def workspace_size(desc: Desc) -> int:
+    return int(lib().mrope_attn_workspace_size(ctypes.byref(desc)))
+
+
+def validate(desc: Desc, q, k, v, pos, gq, gk, seq_lens, out) -> int:
+    """Host-only contract check on raw integer addresses (0 = NULL)."""
+    return int(lib().mrope_attn_validate(ctypes.byref(desc), q, k, v, pos, gq, gk, seq_lens, out))
+
+
+def _bsd_strides(t):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("q/k/v/out must be [B, S, H, D] views with head_dim contiguous")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
+               section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
+               return_lse: bool = False, kprologue="auto", out=None, workspace=None,
+               stage: str = "fwd"):
+    """Fused QK-RMSNorm + 3D M-RoPE joint attention on the current HIP stream.
+
+    q, k, v: [B, S, H, D] bf16 or fp32 GPU tensors (head_dim contiguous; any
+    batch/token/head strides, e.g. views of one fused qkv buffer).
+    pos: [B, S, 3] int32 (t, h, w). gamma_q, gamma_k: [D] fp32.
+    seq_lens: [B] int32 true text lengths (<= text_pad) or None.
+    Returns out [B, S, H, D] (q's dtype), and lse [B, H, S] fp32 if asked.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("pos", pos), ("gamma_q", gamma_q),
+                    ("gamma_k", gamma_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if q.dtype == torch.bfloat16:
+        dt = MRA_BF16
+    elif q.dtype == torch.float32:
+        dt = MRA_FP32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    b, s, h, d = q.shape
+    if tuple(k.shape) != (b, s, h, d) or tuple(v.shape) != (b, s, h, d):
+        raise ValueError("q, k, v shapes differ")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (b, s, 3) or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32 [B, S, 3]")
+    for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if g.dtype != torch.float32 or tuple(g.shape) != (d,) or not g.is_contiguous():
+            raise ValueError(f"{name} must be contiguous float32 [D]")
+    if seq_lens is not None:
+        if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (b,) or not seq_lens.is_cuda:
+            raise ValueError("seq_lens must be a GPU int32 [B] tensor")
+        seq_lens = seq_lens.contiguous()
+    if out is None:
+        out = torch.empty((b, s, h, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((b, h, s), dtype=torch.float32, device=q.device) if return_lse else None
+    desc = make_desc(b, s, h, d, text_pad=text_pad, section=section, theta=theta, eps=eps,
+                     scale=scale, dtype=dt, kprologue=kprologue, q_stride=_bsd_strides(q),
+                     k_stride=_bsd_strides(k), v_stride=_bsd_strides(v), o_stride=_bsd_strides(out))
+    need = workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws = None if not need else workspace.data_ptr()
+    if stage in ("fwd", "attend"):
+        fn = lib().mrope_attn_fwd if stage == "fwd" else lib().mrope_attn_attend
+        rc = fn(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), pos.data_ptr(),
+                gamma_q.data_ptr(), gamma_k.data_ptr(),
+                None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+                None if lse is None else lse.data_ptr(), ws, need, stream)
+    elif stage == "prepare":
+        rc = lib().mrope_attn_prepare(ctypes.byref(desc), k.data_ptr(), pos.data_ptr(),
+                                      gamma_k.data_ptr(), ws, need, stream)
+    else:
+        raise ValueError(f"unknown stage {stage}")
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return (out, lse) if return_lse else out
+
+
+def prepared_call(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, **kw):
+    """(prepare, attend): two closures running the two stages of one call on
+    the current stream with shared output / workspace buffers, so a caller
+    can place events between them (used by the benchmark)."""
+    import torch
+    b, s, h, d = q.shape
+    desc = make_desc(b, s, h, d, text_pad=kw["text_pad"], section=kw.get("section", (16, 24, 24)),
+                     kprologue=kw.get("kprologue", "auto"),
+                     dtype=MRA_BF16 if q.dtype == torch.bfloat16 else MRA_FP32)
+    need = workspace_size(desc)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    common = dict(kw, out=out, workspace=ws)
+
+    def prepare():
+        return mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens, stage="prepare", **common)
+
+    def attend():
+        return mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens, stage="attend", **common)
+
+    return prepare, attend, out

@@ -1,0 +1,247 @@
+// C ABI of libmrope_attn.so: argument validation, workspace sizing, kernel
+// selection and launch on the caller's stream. The operation and the
+// conventions are documented in include/mrope_attn.h.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mrope_attn.h"
+#include "attn_bf16.hpp"
+#include "attn_fp32.hpp"
+#include "prologue.hpp"
+
+namespace {
+
+using mra::Args;
+
+constexpr int kWaves = 4;
+constexpr int kBlockN = 64;
+constexpr int kBlockM = kWaves * 32;
+constexpr int kFp32BlockM = 64;
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int resolve_kprologue(const mra_desc* d) {
+  return d->kprologue == MRA_KPRO_AUTO ? MRA_KPRO_PREPASS : d->kprologue;
+}
+
+// Descriptor-only checks (no pointers).
+int check_desc(const mra_desc* d) {
+  if (!d) return MRA_ERR_NULL;
+  if (d->batch < 0 || d->seq < 0 || d->heads < 1) return MRA_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return MRA_ERR_SHAPE;
+  if (d->text_pad < 0 || d->text_pad > d->seq) return MRA_ERR_SHAPE;
+  if ((int64_t)d->batch * d->seq > (int64_t)1 << 30) return MRA_ERR_SHAPE;
+  if (d->dtype != MRA_BF16 && d->dtype != MRA_FP32) return MRA_ERR_DTYPE;
+  const int half = d->head_dim / 2;
+  if (d->section[0] < 0 || d->section[1] < 0 || d->section[2] < 0 ||
+      (int64_t)d->section[0] + d->section[1] + d->section[2] != half)
+    return MRA_ERR_SECTION;
+  if (!(d->theta > 0.f) || !std::isfinite(d->theta)) return MRA_ERR_PARAM;
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
+  if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
+  if (d->dtype == MRA_BF16 && d->kprologue != MRA_KPRO_AUTO && d->kprologue != MRA_KPRO_FUSED &&
+      d->kprologue != MRA_KPRO_PREPASS)
+    return MRA_ERR_PARAM;
+  return MRA_OK;
+}
+
+int check_strides(const int64_t* st, int dtype) {
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0) return MRA_ERR_STRIDE;
+  if (dtype == MRA_BF16)
+    for (int i = 0; i < 3; ++i)
+      if (st[i] % 8 != 0) return MRA_ERR_STRIDE;
+  return MRA_OK;
+}
+
+// Workspace layout (bf16 path): the (cos, sin) table [B, S, D/2] float2 at
+// offset 0, then, for the prepass K prologue, K' [B, H, S, D] bf16.
+size_t table_bytes(const mra_desc* d) {
+  return round_up((size_t)d->batch * d->seq * (d->head_dim / 2) * sizeof(float2), kWsAlign);
+}
+
+size_t workspace_bytes(const mra_desc* d) {
+  if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0) return 0;
+  size_t n = table_bytes(d);
+  if (resolve_kprologue(d) == MRA_KPRO_PREPASS)
+    n += round_up((size_t)d->batch * d->seq * d->heads * d->head_dim * sizeof(uint16_t), kWsAlign);
+  return n;
+}
+
+void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const void* v,
+               const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
+               void* out, float* lse) {
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.pos = pos; a.gq = gq; a.gk = gk; a.seq_lens = seq_lens;
+  a.out = out; a.lse = lse;
+  a.qs0 = d->q_stride[0]; a.qs1 = d->q_stride[1]; a.qs2 = d->q_stride[2];
+  a.ks0 = d->k_stride[0]; a.ks1 = d->k_stride[1]; a.ks2 = d->k_stride[2];
+  a.vs0 = d->v_stride[0]; a.vs1 = d->v_stride[1]; a.vs2 = d->v_stride[2];
+  a.os0 = d->o_stride[0]; a.os1 = d->o_stride[1]; a.os2 = d->o_stride[2];
+  a.B = d->batch; a.S = d->seq; a.H = d->heads; a.T = d->text_pad;
+  a.eps = d->eps;
+  a.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  a.c2 = (float)((double)a.scale * 1.4426950408889634);
+  const int half = d->head_dim / 2;
+  for (int j = 0; j < half; ++j)
+    a.rope.inv_freq[j] = (float)std::pow((double)d->theta, -2.0 * j / d->head_dim);
+  a.rope.sec_t = d->section[0];
+  a.rope.sec_th = d->section[0] + d->section[1];
+}
+
+template <int D>
+hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
+  const int64_t tokens = (int64_t)a.B * a.S;
+  if (kpro == MRA_KPRO_PREPASS) {
+    hipLaunchKernelGGL(mra::k_prologue_kernel<D>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, a);
+  } else {
+    const int64_t n = tokens * (D / 2);
+    hipLaunchKernelGGL(mra::rope_table_kernel<D>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attend_bf16(Args& a, int kpro, hipStream_t s) {
+  a.n_qt = (a.S + kBlockM - 1) / kBlockM;
+  a.grid = a.B * a.H * a.n_qt;
+  if (kpro == MRA_KPRO_PREPASS)
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, false>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, true>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fp32(Args& a, hipStream_t s) {
+  a.n_qt = (a.S + kFp32BlockM - 1) / kFp32BlockM;
+  a.grid = a.B * a.H * a.n_qt;
+  hipLaunchKernelGGL(mra::attn_fp32_kernel<D>, dim3(a.grid), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mrope_attn_abi_version(void) { return 100; }
+
+const char* mrope_attn_status_string(int status) {
+  switch (status) {
+    case MRA_OK: return "ok";
+    case MRA_ERR_NULL: return "a required pointer is NULL";
+    case MRA_ERR_SHAPE: return "shape out of range (batch/seq/heads/head_dim/text_pad)";
+    case MRA_ERR_DTYPE: return "unknown dtype";
+    case MRA_ERR_SECTION: return "rotary section entries must be >= 0 and sum to head_dim/2";
+    case MRA_ERR_STRIDE: return "unusable strides or alignment";
+    case MRA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MRA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MRA_ERR_HIP: return "HIP launch or runtime error";
+    case MRA_ERR_PARAM: return "invalid theta/eps/softmax_scale/kprologue";
+    default: return "unknown status";
+  }
+}
+
+int mrope_attn_validate(const mra_desc* d, const void* q, const void* k, const void* v,
+                        const int32_t* pos, const float* gq, const float* gk,
+                        const int32_t* seq_lens, const void* out) {
+  (void)seq_lens;
+  int rc = check_desc(d);
+  if (rc != MRA_OK) return rc;
+  if (d->batch == 0 || d->seq == 0) return MRA_OK;
+  if (!q || !k || !v || !pos || !gq || !gk || !out) return MRA_ERR_NULL;
+  if ((rc = check_strides(d->q_stride, d->dtype)) != MRA_OK) return rc;
+  if ((rc = check_strides(d->k_stride, d->dtype)) != MRA_OK) return rc;
+  if ((rc = check_strides(d->v_stride, d->dtype)) != MRA_OK) return rc;
+  if ((rc = check_strides(d->o_stride, d->dtype)) != MRA_OK) return rc;
+  const size_t al = d->dtype == MRA_BF16 ? 16 : 4;
+  if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(out, al)) return MRA_ERR_STRIDE;
+  if (!aligned(pos, 4) || !aligned(seq_lens, 4)) return MRA_ERR_STRIDE;
+  if (!aligned(gq, al) || !aligned(gk, al)) return MRA_ERR_STRIDE;
+  return MRA_OK;
+}
+
+size_t mrope_attn_workspace_size(const mra_desc* d) {
+  if (check_desc(d) != MRA_OK) return 0;
+  return workspace_bytes(d);
+}
+
+// Shared front half of the three launching entry points: validation,
+// workspace check, fault-injection hook and argument packing.
+static int prepare_call(const mra_desc* d, const void* q, const void* k, const void* v,
+                        const int32_t* pos, const float* gq, const float* gk,
+                        const int32_t* seq_lens, void* out, float* lse, void* workspace,
+                        size_t ws_bytes, Args& a, bool& empty) {
+  int rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
+  if (rc != MRA_OK) return rc;
+  empty = d->batch == 0 || d->seq == 0;
+  if (empty) return MRA_OK;
+  if (lse && !aligned(lse, 4)) return MRA_ERR_STRIDE;
+  const size_t need = workspace_bytes(d);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  fill_args(a, d, q, k, v, pos, gq, gk, seq_lens, out, lse);
+  if (d->dtype == MRA_BF16) {
+    a.cs = (float2*)workspace;
+    if (resolve_kprologue(d) == MRA_KPRO_PREPASS) a.kp = (uint16_t*)((char*)workspace + table_bytes(d));
+  }
+  return MRA_OK;
+}
+
+int mrope_attn_prepare(const mra_desc* d, const void* k, const int32_t* pos, const float* gk,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  // q/v/out/gamma_q are not touched by this stage; validate with k standing in
+  Args a;
+  bool empty = false;
+  int rc = prepare_call(d, k, k, k, pos, gk, gk, nullptr, (void*)k, nullptr, workspace, ws_bytes, a, empty);
+  if (rc != MRA_OK || empty || d->dtype != MRA_BF16) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int kpro = resolve_kprologue(d);
+  hipError_t e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
+  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+int mrope_attn_attend(const mra_desc* d, const void* q, const void* k, const void* v,
+                      const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
+                      void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  Args a;
+  bool empty = false;
+  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, empty);
+  if (rc != MRA_OK || empty) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d->dtype == MRA_FP32) {
+    e = d->head_dim == 128 ? launch_fp32<128>(a, s) : launch_fp32<64>(a, s);
+  } else {
+    const int kpro = resolve_kprologue(d);
+    e = d->head_dim == 128 ? launch_attend_bf16<128>(a, kpro, s) : launch_attend_bf16<64>(a, kpro, s);
+  }
+  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* v,
+                   const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
+                   void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  Args a;
+  bool empty = false;
+  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, empty);
+  if (rc != MRA_OK || empty) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d->dtype == MRA_FP32) {
+    e = d->head_dim == 128 ? launch_fp32<128>(a, s) : launch_fp32<64>(a, s);
+  } else {
+    const int kpro = resolve_kprologue(d);
+    e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
+    if (e == hipSuccess)
+      e = d->head_dim == 128 ? launch_attend_bf16<128>(a, kpro, s) : launch_attend_bf16<64>(a, kpro, s);
+  }
+  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+/*
+ * mrope_attn.h -- C ABI of the fused QK-RMSNorm + 3D M-RoPE joint text+image
+ * attention library for AMD Instinct MI355X (gfx950), libmrope_attn.so.
+ *
+ * The operation (Ideogram 4.0 announcement thread, the post listing the DiT's
+ * parts: single-stream self-attention with QK-RMSNorm and a 3D multimodal RoPE
+ * that puts text and image tokens in one positional frame; "Ideogram 4 deep
+ * dive", section 4 part 2: text and image tokens concatenated into one
+ * sequence through the same self-attention), for every batch item b, head h
+ * and token s of a sequence of S = text_pad + image tokens:
+ *
+ *   1. RMSNorm over head_dim:  x_hat = x * (mean_d x_d^2 + eps)^-1/2 * gamma
+ *      (gamma_q for Q, gamma_k for K; one [head_dim] weight shared by heads);
+ *   2. 3D M-RoPE: rotary pair j = (x_hat_j, x_hat_{j+D/2}), j < D/2, is turned
+ *      by pos[b,s,axis(j)] * theta^(-2j/D), where axis(j) is t for the first
+ *      section[0] pairs, h for the next section[1], w for the last section[2]
+ *      ("Ideogram 4 deep dive", section 6 part 3 names the split (24,20,20));
+ *      the frequency is computed in fp32 (the unsloth commit log for the
+ *      Ideogram 4 backend: rotary inv_freq is built in explicit fp32);
+ *   3. non-causal softmax attention with scale softmax_scale over the valid
+ *      keys of the item; text slot s < text_pad is valid iff s < seq_lens[b]
+ *      (per-prompt true text length, padded in memory: SimpleTuner
+ *      quickstart, "Text Embed Cache"); image tokens are always valid.
+ *      Output rows of invalid tokens are written as exact zeros.
+ *
+ * Numerics of the bf16 path: fp32 norm/rotation math, Q' and K' rounded once
+ * to bf16 (round-to-nearest-even), bf16 x bf16 -> fp32 matrix-core products,
+ * fp32 online softmax, probabilities rounded once to bf16 before P.V (the row
+ * sum uses the same rounded values), output rounded once. The fp32 path
+ * rounds nowhere beyond fp32 arithmetic.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE memory owned by the caller; the library
+ *    keeps no pointer after a call returns and never frees caller memory.
+ *  - q, k, v, out are [B, S, H, D] views with head_dim contiguous and element
+ *    strides given for the batch, token and head axes (so Q, K, V may be
+ *    strided views of one fused [B, S, 3, H, D] projection output -- the
+ *    Ideogram 4 checkpoint stores Q/K/V rows stacked in one fused weight, per
+ *    the unsloth commit log; Q, K and V have the same head count there).
+ *  - pos_thw is [B, S, 3] int32 contiguous, (t, h, w) per token.
+ *  - gamma_q, gamma_k are [D] fp32. seq_lens is [B] int32 or NULL (no
+ *    padding); values are read on the device and clamped to [0, text_pad].
+ *  - lse, when not NULL, is [B, H, S] fp32 contiguous: natural-log
+ *    log-sum-exp of the scaled logits of each valid row, -inf for invalid rows.
+ *  - stream is a hipStream_t (NULL = the legacy default stream). Calls are
+ *    asynchronous; results are valid after the stream synchronises.
+ *  - Errors are negative mra_status values. Every contract check runs on the
+ *    host before any device work; on error nothing is launched or written.
+ *  - Calls are thread-safe; the library holds no global state.
+ */
+#ifndef MROPE_ATTN_H
+#define MROPE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MRA_OK = 0,
+  MRA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MRA_ERR_SHAPE = -2,       /* batch/seq/heads/head_dim/text_pad out of range */
+  MRA_ERR_DTYPE = -3,       /* unknown dtype */
+  MRA_ERR_SECTION = -4,     /* section entries negative or not summing to D/2 */
+  MRA_ERR_STRIDE = -5,      /* strides/alignment unusable (see mra_desc) */
+  MRA_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
+  MRA_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
+  MRA_ERR_HIP = -8,         /* a HIP launch or runtime call failed */
+  MRA_ERR_PARAM = -9        /* theta/eps/scale/kprologue invalid */
+} mra_status;
+
+typedef enum { MRA_BF16 = 0, MRA_FP32 = 1 } mra_dtype;
+
+/* Where the K prologue (RMSNorm + M-RoPE of K) runs in the bf16 path. */
+typedef enum {
+  MRA_KPRO_AUTO = 0,    /* library's choice (currently MRA_KPRO_PREPASS) */
+  MRA_KPRO_FUSED = 1,   /* applied while each K tile is staged into LDS */
+  MRA_KPRO_PREPASS = 2  /* one pass writes K' (bf16) to the workspace first */
+} mra_kprologue;
+
+typedef struct {
+  int32_t batch;          /* B >= 0 (0 = nothing to do) */
+  int32_t seq;            /* S >= 0: text_pad text slots, then image tokens */
+  int32_t heads;          /* H >= 1, same for Q, K, V */
+  int32_t head_dim;       /* D: 64 or 128 */
+  int32_t text_pad;       /* text slots at the start of each sequence, 0..S */
+  int32_t section[3];     /* rotary pairs driven by t, h, w; sum == D/2 */
+  float theta;            /* rotary base, > 0 (10000) */
+  float eps;              /* RMSNorm epsilon, >= 0 (1e-6) */
+  float softmax_scale;    /* > 0, or <= 0 for 1/sqrt(D) */
+  int32_t dtype;          /* mra_dtype of q, k, v and out */
+  int32_t kprologue;      /* mra_kprologue (bf16 only; ignored for fp32) */
+  int64_t q_stride[3];    /* element strides of the batch, token, head axes */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} mra_desc;
+
+/* Host-only check of a call's arguments; touches no device and reads no
+ * device memory. Returns MRA_OK or the error mrope_attn_fwd would return.
+ * bf16 requires 16-byte aligned q, k, v, out, gamma_q, gamma_k and
+ * token/head/batch strides that are multiples of 8 elements; fp32 requires
+ * 4-byte alignment. */
+int mrope_attn_validate(const mra_desc* desc, const void* q, const void* k, const void* v,
+                        const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                        const int32_t* seq_lens, const void* out);
+
+/* Bytes of device workspace mrope_attn_fwd needs for this descriptor
+ * (0 when none). Returns 0 for an invalid descriptor. */
+size_t mrope_attn_workspace_size(const mra_desc* desc);
+
+/* The fused forward pass (see the top of this file). workspace must hold at
+ * least mrope_attn_workspace_size(desc) bytes (16-byte aligned) when that
+ * size is nonzero; it is scratch, overwritten by the call. out must not
+ * overlap q, k, v or the workspace. Launches on `stream` and returns without
+ * synchronising. */
+int mrope_attn_fwd(const mra_desc* desc, const void* q, const void* k, const void* v,
+                   const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                   const int32_t* seq_lens, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of mrope_attn_fwd, for callers that schedule or time them
+ * separately. mrope_attn_prepare runs the prologue pass (the per-token
+ * rotary (cos, sin) table, plus K' for MRA_KPRO_PREPASS) into the workspace;
+ * it reads only k, pos_thw and gamma_k (a no-op for fp32). mrope_attn_attend
+ * then runs the attention kernel and requires that mrope_attn_prepare has run
+ * on the same stream (or been ordered before it) with the same descriptor,
+ * inputs and workspace. fwd == prepare followed by attend. Arguments,
+ * validation and errors are as for mrope_attn_fwd. */
+int mrope_attn_prepare(const mra_desc* desc, const void* k, const int32_t* pos_thw,
+                       const float* gamma_k, void* workspace, size_t workspace_bytes,
+                       void* stream);
+int mrope_attn_attend(const mra_desc* desc, const void* q, const void* k, const void* v,
+                      const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                      const int32_t* seq_lens, void* out, float* lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* mrope_attn_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int mrope_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MROPE_ATTN_H */

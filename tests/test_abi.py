@@ -1,0 +1,186 @@
+"""C ABI contract on the CPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any device work.
+
+No compute call runs here (there is no GPU); the calls below either fail
+validation, take the empty-input early return, or stop at the fault-injection
+hook that sits just before the first launch.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from diffusion_transformer_image_head_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mrope_attn.h")
+
+FAKE = 0x10000  # aligned, non-null; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from diffusion_transformer_image_head_amd.build import build
+        build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(mrope_attn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_fwd", "mrope_attn_prepare",
+        "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_workspace_size"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True)
+    exported = set(l.split()[-1] for l in out.stdout.splitlines() if l.strip())
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_desc_layout_matches_header(lib):
+    # 11 int32/float fields + 3 + 12 int64 strides; int64 block aligned at 8
+    assert ctypes.sizeof(B.Desc) == 4 * 13 + 4 + 8 * 12
+    assert B.Desc.q_stride.offset == 56
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mrope_attn_abi_version() == 100
+    for st in range(0, -10, -1):
+        s = B.status_string(st)
+        assert s and s != "unknown status"
+    assert B.status_string(-77) == "unknown status"
+
+
+def desc(**kw):
+    base = dict(batch=2, seq=100, heads=4, head_dim=128, text_pad=20)
+    base.update(kw)
+    args = {k: base.pop(k) for k in ("batch", "seq", "heads", "head_dim")}
+    return B.make_desc(args["batch"], args["seq"], args["heads"], args["head_dim"], **base)
+
+
+def val(d, **ptr):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, pos=FAKE, gq=FAKE, gk=FAKE, seq=None, out=FAKE)
+    p.update(ptr)
+    return B.validate(d, p["q"], p["k"], p["v"], p["pos"], p["gq"], p["gk"], p["seq"], p["out"])
+
+
+def test_validate_accepts_good_calls(lib):
+    assert val(desc()) == 0
+    assert val(desc(section=(24, 20, 20))) == 0
+    assert val(desc(head_dim=64, section=(8, 12, 12))) == 0
+    assert val(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
+    assert val(desc(text_pad=0)) == 0
+    assert val(desc(text_pad=100)) == 0
+    assert val(desc(), seq=FAKE) == 0
+    # strided views of one fused [B, S, 3, H, D] qkv buffer
+    st = (100 * 3 * 4 * 128, 3 * 4 * 128, 128)
+    assert val(desc(q_stride=st, k_stride=st, v_stride=st)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96, section=(16, 16, 16)), -2),
+    (dict(head_dim=32, section=(4, 6, 6)), -2),
+    (dict(heads=0), -2),
+    (dict(batch=-1), -2),
+    (dict(text_pad=101), -2),
+    (dict(text_pad=-1), -2),
+    (dict(dtype=7), -3),
+    (dict(section=(16, 24, 23)), -4),
+    (dict(section=(-1, 33, 32)), -4),
+    (dict(theta=0.0), -9),
+    (dict(theta=float("nan")), -9),
+    (dict(eps=-1e-6), -9),
+    (dict(scale=float("inf")), -9),
+    (dict(kprologue=5), -9),
+    (dict(q_stride=(100 * 4 * 128, 4 * 128, 100)), -5),     # bf16 needs multiples of 8
+    (dict(o_stride=(-1, 4 * 128, 128)), -5),
+])
+def test_validate_rejects(lib, kw, code):
+    assert val(desc(**kw)) == code
+
+
+def test_validate_pointers(lib):
+    d = desc()
+    for name in ("q", "k", "v", "pos", "gq", "gk", "out"):
+        assert val(d, **{name: None}) == -1, name
+    assert val(d, q=FAKE + 8) == -5          # bf16 pointers need 16-byte alignment
+    assert val(d, out=FAKE + 2) == -5
+    assert val(d, seq=FAKE + 2) == -5
+    assert B.lib().mrope_attn_validate(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE) == -1
+
+
+def test_empty_inputs_are_noops(lib):
+    for d in (desc(batch=0), desc(seq=0, text_pad=0)):
+        assert val(d, q=None, k=None, v=None, out=None) == 0
+        rc = lib.mrope_attn_fwd(ctypes.byref(d), None, None, None, None, None, None, None,
+                                None, None, None, 0, None)
+        assert rc == 0
+        assert B.workspace_size(d) == 0
+
+
+def test_workspace_sizes(lib):
+    d = desc(batch=1, seq=4608, heads=32, text_pad=512)
+    table = 4608 * 64 * 8
+    kprime = 4608 * 32 * 128 * 2
+    assert B.workspace_size(d) == table + kprime                   # auto = prepass
+    assert B.workspace_size(desc(batch=1, seq=4608, heads=32, text_pad=512,
+                                 kprologue="fused")) == table
+    assert B.workspace_size(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
+    assert B.workspace_size(desc(section=(1, 2, 3))) == 0          # invalid -> 0
+    assert lib.mrope_attn_workspace_size(None) == 0
+
+
+def _fwd(d, ws, nbytes, lse=None):
+    return B.lib().mrope_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                  FAKE, lse, ws, nbytes, None)
+
+
+def test_fwd_rejects_before_launch(lib, monkeypatch):
+    d = desc()
+    need = B.workspace_size(d)
+    assert _fwd(d, None, 0) == -7
+    assert _fwd(d, FAKE, need - 1) == -7
+    assert _fwd(d, FAKE + 4, need) == -7
+    assert _fwd(d, FAKE, need, lse=FAKE + 1) == -5
+    assert _fwd(desc(section=(1, 1, 1)), FAKE, need) == -4
+    # fault injection: everything valid, the call stops right before launching
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _fwd(d, FAKE, need) == -8
+    assert _fwd(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12)), None, 0) == -8
+    L = B.lib()
+    assert L.mrope_attn_prepare(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, None) == -8
+    assert L.mrope_attn_attend(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               None, FAKE, need, None) == -8
+
+
+def test_stages_validate_like_fwd(lib):
+    d = desc()
+    need = B.workspace_size(d)
+    L = B.lib()
+    assert L.mrope_attn_prepare(ctypes.byref(d), None, FAKE, FAKE, FAKE, need, None) == -1
+    assert L.mrope_attn_prepare(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0, None) == -7
+    assert L.mrope_attn_attend(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               None, FAKE, need - 1, None) == -7
+    e = desc(batch=0)
+    assert L.mrope_attn_prepare(ctypes.byref(e), None, None, None, None, 0, None) == 0
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 4, 1, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        B.mrope_attn(x, x, x, torch.zeros(1, 4, 3, dtype=torch.int32), torch.ones(64),
+                     torch.ones(64), text_pad=0, section=(8, 12, 12))
