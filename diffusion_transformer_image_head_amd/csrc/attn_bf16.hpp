@@ -19,18 +19,35 @@
 // Row max / row sum are lane-local plus one permlane32 swap. K' rows are
 // stored in LDS in the order that makes each lane's 16 S^T values 16
 // consecutive keys, so the P fragment feeds P.V directly. V is transposed
-// into LDS ([dim][key]) by an in-register 4x8 transpose during staging.
+// into LDS ([dim][key]) by an in-register transpose during staging.
+//
+// K/V tiles are double-buffered in LDS: tile t+1 is fetched with buffer loads
+// (out-of-range rows read as zero) while tile t is computed, then stored to
+// the other buffer, so each tile costs one workgroup barrier.
+//
+// Softmax runs in the log2 domain with a lazily updated running max: the
+// output accumulators are rescaled only when some row's tile max exceeds its
+// running max by more than kRescaleLog2 (so probabilities stay <= 2^8 before
+// normalisation). The result is the same softmax; only the moment of
+// rescaling changes.
 #pragma once
 
 #include "mra_common.hpp"
 
 namespace mra {
 
+constexpr float kRescaleLog2 = 8.0f;
+constexpr int kBufFlags = 0x00020000;  // raw buffer resource, 32-bit data format
+
 // LDS row of key n (within a 32-key block) so that MFMA output element i of
 // lane half h corresponds to key h * 16 + i.
 __device__ __forceinline__ int key_lds_row(int n) {
   const int blk = n & ~31, w = n & 31;
   return blk | (((w >> 2) & 3) << 3) | ((w >> 4) << 2) | (w & 3);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
 
 template <int D, int WAVES, int BN, bool KFUSED>
@@ -46,11 +63,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   constexpr int KCH = BN * DCH / NT;  // K chunks staged per thread
   constexpr int VKR = BN * DCH / NT;  // V keys per thread's transposed block
   constexpr int VKG = BN / VKR;       // key groups across the workgroup
+  constexpr int KBUF = BN * KP, VBUF = D * VP;
   static_assert(KCH >= 1 && VKR >= 2 && (VKR & 1) == 0, "tile too small for the workgroup");
   static_assert(VKG * DCH == NT, "V staging must cover the tile exactly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
@@ -134,62 +152,76 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     }
   }
 
-  // ---- staging of one K/V tile: global -> registers -> LDS
+  // ---- K/V tile staging: buffer loads -> registers -> LDS (double buffered)
   const int ntiles = (S + BN - 1) / BN;
-  auto skipped = [&](int t) { const int n0 = t * BN; return n0 >= L && n0 + BN <= T; };
+  // a tile with no valid key (all of its in-sequence keys are padded text) is skipped
+  auto skipped = [&](int t) { const int n0 = t * BN; return n0 >= L && min(n0 + BN, S) <= T; };
   auto next_tile = [&](int t) {
     ++t;
     while (t < ntiles && skipped(t)) ++t;
     return t;
   };
 
+  // K rows: K' (dense [S, D] per (b, head)) or raw K (token stride ks1).
+  const int64_t krow = KFUSED ? a.ks1 : D;
   const uint16_t* kbase = KFUSED ? (const uint16_t*)a.k + b * a.ks0 + head * a.ks2
                                  : a.kp + ((int64_t)b * a.H + head) * S * D;
-  const int64_t kstride = KFUSED ? a.ks1 : D;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)(((int64_t)(S - 1) * krow + D) * 2));
   const uint16_t* vbase = (const uint16_t*)a.v + b * a.vs0 + head * a.vs2;
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2));
+
+  // per-thread staging coordinates (fixed for the whole loop)
+  int k_key[KCH], k_dch[KCH], k_off[KCH], k_lds[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int ci = tid + i * NT;
+    k_key[i] = ci / DCH;
+    int dch = ci % DCH;
+    if constexpr (KFUSED) dch = (dch >> 1) + (dch & 1) * (DCH / 2);  // pair partner = lane ^ 1
+    k_dch[i] = dch;
+    k_off[i] = (int)((k_key[i] * krow + dch * 8) * 2);
+    k_lds[i] = key_lds_row(k_key[i]) * KP + dch * 8;
+  }
   const int vkg = tid % VKG, vdc = tid / VKG;
+  const int v_off = (int)(((int64_t)vkg * VKR * a.vs1 + vdc * 8) * 2);
+  const int v_rowb = (int)(a.vs1 * 2);
+  const int v_lds = (vdc * 8) * VP + vkg * VKR;
 
   u32x4 kr[KCH], vr[VKR];
   float2 csr[KFUSED ? KCH : 1][4];
 
   auto load_tile = [&](int t) {
     const int n0 = t * BN;
+    const int ks = (int)(n0 * krow * 2);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * NT;
-      const int key = ci / DCH;
-      int dch = ci % DCH;
-      if constexpr (KFUSED) dch = (dch >> 1) + (dch & 1) * (DCH / 2);  // pair partner = lane ^ 1
-      const int n = n0 + key;
-      kr[i] = n < S ? *(const u32x4*)(kbase + n * kstride + dch * 8) : u32x4{0u, 0u, 0u, 0u};
+      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[i], ks, 0);
       if constexpr (KFUSED) {
-        const int j0 = (dch % (DCH / 2)) * 8;
-        const float2* cp = a.cs + ((int64_t)b * S + min(n, S - 1)) * (D / 2) + j0 + (dch >= DCH / 2 ? 4 : 0);
-        // each lane needs the 8 angles of its pair group; lanes dch and dch^1
-        // share them, so each lane fetches 4 and swaps halves below
+        const int n = min(n0 + k_key[i], S - 1);
+        const int j0 = (k_dch[i] % (DCH / 2)) * 8 + (k_dch[i] >= DCH / 2 ? 4 : 0);
+        const float2* cp = a.cs + ((int64_t)b * S + n) * (D / 2) + j0;
+        // lanes dch and dch^1 share one group of 8 pair angles: each fetches
+        // 4 and the halves are swapped at store time
 #pragma unroll
         for (int e = 0; e < 4; ++e) csr[i][e] = cp[e];
       }
     }
+    const int vs = n0 * v_rowb;
 #pragma unroll
-    for (int i = 0; i < VKR; ++i) {
-      const int n = n0 + vkg * VKR + i;
-      const bool ok = n < S && !(n >= L && n < T);
-      vr[i] = ok ? *(const u32x4*)(vbase + (int64_t)n * a.vs1 + vdc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < VKR; ++i)
+      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * v_rowb, vs, 0);
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int t, int buf) {
+    const int n0 = t * BN;
+    uint16_t* kd = Ks + buf * KBUF;
+    uint16_t* vd = Vt + buf * VBUF;
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * NT;
-      const int key = ci / DCH;
-      int dch = ci % DCH;
       u32x4 w = kr[i];
       if constexpr (KFUSED) {
-        dch = (dch >> 1) + (dch & 1) * (DCH / 2);
-        // RMSNorm over the 16 lanes holding this key row, then rotate pairs
-        // (lane holding chunk c < DCH/2 has x1, its neighbour lane^1 has x2).
+        // RMSNorm over the lanes holding this key row, then rotate pairs
+        // (the lane holding chunk c < DCH/2 has x1, its neighbour lane^1 x2).
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[2 * e] = bf16_lo(w[e]); x[2 * e + 1] = bf16_hi(w[e]); }
@@ -197,13 +229,13 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
-        for (int x = 1; x < DCH; x <<= 1) ss += __shfl_xor(ss, x, DCH);
+        for (int s = 1; s < DCH; s <<= 1) ss += __shfl_xor(ss, s, DCH);
         const float r = rsqrtf(ss * (1.0f / D) + a.eps);
+        const int dch = k_dch[i];
         const bool first = dch < DCH / 2;
-        const int gofs = dch * 8;
         float y[8], px[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * a.gk[gofs + e];
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * a.gk[dch * 8 + e];
 #pragma unroll
         for (int e = 0; e < 8; ++e) px[e] = __shfl_xor(y[e], 1, 64);
         float2 cs8[8];
@@ -222,9 +254,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
       }
-      *(u32x4*)&Ks[key_lds_row(key) * KP + dch * 8] = w;
+      *(u32x4*)&kd[k_lds[i]] = w;
     }
-    // V: VKR keys x 8 dims -> 8 rows of V^T, VKR keys each
+    // V rows of padded text keys (and rows past the end) become zeros so a
+    // non-finite value there cannot reach P.V (their P is exactly 0).
+    if (n0 + BN > S || (n0 + BN > L && n0 < T)) {
+#pragma unroll
+      for (int i = 0; i < VKR; ++i) {
+        const int n = n0 + vkg * VKR + i;
+        if (n >= S || (n >= L && n < T)) vr[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // VKR keys x 8 dims -> 8 rows of V^T, VKR keys each
 #pragma unroll
     for (int d2 = 0; d2 < 4; ++d2) {
       uint32_t lo[VKR / 2], hi[VKR / 2];
@@ -233,7 +274,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
         lo[i / 2] = __builtin_amdgcn_perm(vr[i + 1][d2], vr[i][d2], 0x05040100u);
         hi[i / 2] = __builtin_amdgcn_perm(vr[i + 1][d2], vr[i][d2], 0x07060302u);
       }
-      uint16_t* r0 = &Vt[(vdc * 8 + 2 * d2) * VP + vkg * VKR];
+      uint16_t* r0 = vd + v_lds + 2 * d2 * VP;
       uint16_t* r1 = r0 + VP;
       if constexpr (VKR == 4) {
         *(u32x2*)r0 = u32x2{lo[0], lo[1]};
@@ -255,16 +296,20 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
 
   int t = 0;
   while (t < ntiles && skipped(t)) ++t;
-  if (t < ntiles) load_tile(t);
+  int buf = 0;
+  if (t < ntiles) {
+    load_tile(t);
+    store_tile(t, 0);
+  }
+  __syncthreads();
 
-  for (; t < ntiles;) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
+  while (t < ntiles) {
     const int tn = next_tile(t);
     if (tn < ntiles) load_tile(tn);
 
     const int n0 = t * BN;
+    const uint16_t* kc = Ks + buf * KBUF;
+    const uint16_t* vc = Vt + buf * VBUF;
     // S^T = K' Q'^T for each 32-key block
     f32x16 st[NB];
 #pragma unroll
@@ -273,13 +318,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
       for (int i = 0; i < 16; ++i) st[kb][i] = 0.f;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const bf16x8 av = *(const bf16x8*)&Ks[(kb * 32 + m) * KP + c * 16 + hf * 8];
+        const bf16x8 av = *(const bf16x8*)&kc[(kb * 32 + m) * KP + c * 16 + hf * 8];
         st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], st[kb], 0, 0, 0);
       }
     }
     // key-padding / sequence-end mask (select, so NaN in masked keys cannot leak)
-    const bool need_mask = (n0 + BN > S) || (n0 + BN > L && n0 < T);
-    if (need_mask) {
+    if (n0 + BN > S || (n0 + BN > L && n0 < T)) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -289,31 +333,31 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
           st[kb][i] = ok ? st[kb][i] : -INFINITY;
         }
     }
-    // online softmax in the log2 domain
+    // online softmax in the log2 domain, lazily rescaled
     float mx = st[0][0];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][i]);
-    mx = half_swap_max(mx);
-    const float mnew = fmaxf(mrun, mx * c2);
-    const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-    mrun = mnew;
-    lrun *= alpha;
+    mx = half_swap_max(mx) * c2;
+    if (__builtin_amdgcn_ballot_w64(mx > mrun + kRescaleLog2) != 0) {
+      const float mnew = fmaxf(mrun, mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      lrun *= alpha;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
     bf16x8 pf[NB][2];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][u * 8 + e], c2, -mnew));
-          pf[kb][u][e] = (__bf16)p;
-        }
+        for (int e = 0; e < 8; ++e)
+          pf[kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][u * 8 + e], c2, -mrun));
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pp = {pf[kb][u][e], pf[kb][u][e + 1]};
@@ -327,9 +371,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 av = *(const bf16x8*)&Vt[(db * 32 + m) * VP + kb * 32 + hf * 16 + u * 8];
+          const bf16x8 av = *(const bf16x8*)&vc[(db * 32 + m) * VP + kb * 32 + hf * 16 + u * 8];
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[kb][u], oacc[db], 0, 0, 0);
         }
+    if (tn < ntiles) store_tile(tn, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
     t = tn;
   }
 

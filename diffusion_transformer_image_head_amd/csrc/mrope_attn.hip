@@ -158,6 +158,14 @@ int mrope_attn_validate(const mra_desc* d, const void* q, const void* k, const v
   if ((rc = check_strides(d->k_stride, d->dtype)) != MRA_OK) return rc;
   if ((rc = check_strides(d->v_stride, d->dtype)) != MRA_OK) return rc;
   if ((rc = check_strides(d->o_stride, d->dtype)) != MRA_OK) return rc;
+  // the bf16 kernels address each (batch, head) slice with 32-bit byte offsets
+  if (d->dtype == MRA_BF16) {
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t* st[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+    for (int i = 0; i < 4; ++i)
+      if (((int64_t)d->seq * st[i][1] + d->head_dim) * 2 >= lim) return MRA_ERR_UNSUPPORTED;
+    if ((int64_t)d->seq * d->head_dim * 2 >= lim) return MRA_ERR_UNSUPPORTED;
+  }
   const size_t al = d->dtype == MRA_BF16 ? 16 : 4;
   if (!aligned(q, al) || !aligned(k, al) || !aligned(v, al) || !aligned(out, al)) return MRA_ERR_STRIDE;
   if (!aligned(pos, 4) || !aligned(seq_lens, 4)) return MRA_ERR_STRIDE;

@@ -107,6 +107,7 @@ def test_validate_accepts_good_calls(lib):
     (dict(kprologue=5), -9),
     (dict(q_stride=(100 * 4 * 128, 4 * 128, 100)), -5),     # bf16 needs multiples of 8
     (dict(o_stride=(-1, 4 * 128, 128)), -5),
+    (dict(seq=1 << 20, text_pad=0, k_stride=(0, 1 << 11, 128)), -6),   # > 2 GiB per slice
 ])
 def test_validate_rejects(lib, kw, code):
     assert val(desc(**kw)) == code
