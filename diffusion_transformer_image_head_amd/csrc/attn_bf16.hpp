@@ -14,22 +14,27 @@
 // so a query row lives in one lane pair (lanes m and m + 32):
 //   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, A = K' from LDS,
 //                                    B = Q' from registers;
-//   O^T (dims x queries) += V^T P^T  same MFMA, A = V^T from LDS, B = P from
-//                                    the S^T accumulators (no LDS round trip).
-// Row max / row sum are lane-local plus one permlane32 swap. K' rows are
-// stored in LDS in the order that makes each lane's 16 S^T values 16
-// consecutive keys, so the P fragment feeds P.V directly. V is transposed
-// into LDS ([dim][key]) by an in-register transpose during staging.
+//   O^T (dims x queries) += V^T P^T  same MFMA, A = V^T read from LDS with the
+//                                    gfx950 transposing LDS read, B = P taken
+//                                    straight from the S^T accumulators.
+// Row max / row sum are lane-local plus one permlane32 swap.
 //
-// K/V tiles are double-buffered in LDS: tile t+1 is fetched with buffer loads
-// (out-of-range rows read as zero) while tile t is computed, then stored to
-// the other buffer, so each tile costs one workgroup barrier.
+// LDS: K' and V tiles arrive by buffer loads that write LDS directly (lane L of
+// a load lands at 16*L of a 1 KiB run), with 16-byte chunks XOR-swizzled per
+// row so the matrix-operand reads are free of bank conflicts. K' rows sit in
+// the order that makes each lane's 16 S^T values 16 consecutive keys, so the P
+// fragment feeds P.V directly. K' and V are double-buffered and staggered by
+// one tile: after each tile's barrier the loads of K'(t+2) and V(t+1) are
+// issued, then Q.K'(t+1) is issued before the softmax of tile t so the matrix
+// cores run while the vector ALUs do the exponentials.
 //
-// Softmax runs in the log2 domain with a lazily updated running max: the
-// output accumulators are rescaled only when some row's tile max exceeds its
-// running max by more than kRescaleLog2 (so probabilities stay <= 2^8 before
-// normalisation). The result is the same softmax; only the moment of
-// rescaling changes.
+// Numerics: Q' is rounded to bf16 already multiplied by softmax_scale*log2(e),
+// so S^T is in log2 units; the S^T accumulators start at -m (the running row
+// max), which makes P = exp2(S^T) with no further arithmetic. The running max
+// is updated lazily: only when some row's tile max exceeds it by more than
+// kRescaleLog2 are the output accumulators rescaled (probabilities stay below
+// 2^8 before normalisation). The row sum adds the bf16-rounded P, the same
+// values P.V uses.
 #pragma once
 
 #include "mra_common.hpp"
@@ -39,36 +44,44 @@ namespace mra {
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource, 32-bit data format
 
-// LDS row of key n (within a 32-key block) so that MFMA output element i of
-// lane half h corresponds to key h * 16 + i.
-__device__ __forceinline__ int key_lds_row(int n) {
-  const int blk = n & ~31, w = n & 31;
-  return blk | (((w >> 2) & 3) << 3) | ((w >> 4) << 2) | (w & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Key held by LDS row r of a 32-row block: rows are ordered so that MFMA
+// output element i of lane half h is key h * 16 + i.
+__device__ __forceinline__ int key_of_row(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
 
+// Byte offset inside a swizzled LDS tile of logical 16-byte chunk c of row r.
+// K' tiles XOR the chunk with (r & 7); V tiles with 2 * (r & 3).
+template <int D>
+__device__ __forceinline__ int k_lds_off(int r, int c) { return r * (D * 2) + ((c ^ (r & 7)) << 4); }
+template <int D>
+__device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4); }
+
 template <int D, int WAVES, int BN, bool KFUSED>
 __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   constexpr int BM = WAVES * 32;
   constexpr int NT = WAVES * 64;
-  constexpr int KC = D / 16;          // 16-wide head_dim chunks (QK^T k-steps)
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int NB = BN / 32;         // 32-key blocks per tile
-  constexpr int KP = D + 8;           // LDS pitch of K' rows (elements)
-  constexpr int VP = BN + 8;          // LDS pitch of V^T rows (elements)
-  constexpr int DCH = D / 8;          // 8-element chunks per row
-  constexpr int KCH = BN * DCH / NT;  // K chunks staged per thread
-  constexpr int VKR = BN * DCH / NT;  // V keys per thread's transposed block
-  constexpr int VKG = BN / VKR;       // key groups across the workgroup
-  constexpr int KBUF = BN * KP, VBUF = D * VP;
-  static_assert(KCH >= 1 && VKR >= 2 && (VKR & 1) == 0, "tile too small for the workgroup");
-  static_assert(VKG * DCH == NT, "V staging must cover the tile exactly");
+  constexpr int KC = D / 16;                 // 16-wide head_dim chunks (QK^T k-steps)
+  constexpr int DB = D / 32;                 // 32-row blocks of O^T
+  constexpr int NB = BN / 32;                // 32-key blocks per tile
+  constexpr int ROWB = D * 2;                // bytes per LDS row
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
+  constexpr int RUNS = TILEB / 1024 / WAVES; // 1 KiB direct-load runs per wave per tile
+  constexpr int RPR = 1024 / ROWB;           // rows per run
+  constexpr int KCH = BN * CPR / NT;         // fused mode: K chunks per thread
+  static_assert(RUNS >= 1 && RUNS * WAVES * 1024 == TILEB, "tile must split into whole runs");
+  static_assert(KCH >= 1 && KCH * NT == BN * CPR, "fused staging must cover the tile");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
+  __shared__ __attribute__((aligned(1024))) char Ksm[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) char Vsm[2 * TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
@@ -99,8 +112,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     return;
   }
 
-  // ---- Q prologue: RMSNorm + M-RoPE in fp32, one bf16 rounding, kept as the
-  // B operand of S^T: lane (m, hf) holds Q'[row][c*16 + hf*8 + e].
+  // ---- Q prologue: RMSNorm + M-RoPE in fp32, scaled by softmax_scale*log2(e),
+  // one bf16 rounding, kept as the B operand of S^T: lane (m, hf) holds
+  // Q'[row][c*16 + hf*8 + e].
   bf16x8 qf[KC];
   {
     float x[KC][8];
@@ -128,6 +142,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
       for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
     ss = half_swap_sum(ss);
     const float r = rsqrtf(ss * (1.0f / D) + a.eps);
+    const float c2 = a.c2;
     // (cos, sin) of this token's pairs from the table the prologue pass wrote
     const float2* csrow = a.cs + ((int64_t)b * S + min(row, S - 1)) * (D / 2);
 #pragma unroll
@@ -146,82 +161,97 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
         const float cs = t4[e >> 1][(e & 1) * 2], sn = t4[e >> 1][(e & 1) * 2 + 1];
         const float u = x[c][e] * r * g1;
         const float w = x[c + KC / 2][e] * r * g2;
-        qf[c][e] = (__bf16)(u * cs - w * sn);
-        qf[c + KC / 2][e] = (__bf16)(w * cs + u * sn);
+        qf[c][e] = (__bf16)((u * cs - w * sn) * c2);
+        qf[c + KC / 2][e] = (__bf16)((w * cs + u * sn) * c2);
       }
     }
   }
 
-  // ---- K/V tile staging: buffer loads -> registers -> LDS (double buffered)
+  // ---- tile bookkeeping: tiles with no valid key are skipped
   const int ntiles = (S + BN - 1) / BN;
-  // a tile with no valid key (all of its in-sequence keys are padded text) is skipped
   auto skipped = [&](int t) { const int n0 = t * BN; return n0 >= L && min(n0 + BN, S) <= T; };
   auto next_tile = [&](int t) {
     ++t;
     while (t < ntiles && skipped(t)) ++t;
     return t;
   };
+  auto tile_masked = [&](int n0) { return n0 + BN > S || (L < T && n0 + BN > L && n0 < T); };
+  auto key_ok = [&](int n) { return n < S && !(n >= L && n < T); };
 
-  // K rows: K' (dense [S, D] per (b, head)) or raw K (token stride ks1).
-  const int64_t krow = KFUSED ? a.ks1 : D;
+  // ---- operand sources. All bounds live in the per-lane offset: a row that
+  // must not be read gets an offset at the resource size, which reads zeros.
+  const int64_t krow = KFUSED ? a.ks1 : D;  // elements between K rows
   const uint16_t* kbase = KFUSED ? (const uint16_t*)a.k + b * a.ks0 + head * a.ks2
                                  : a.kp + ((int64_t)b * a.H + head) * S * D;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, (uint32_t)(((int64_t)(S - 1) * krow + D) * 2));
+  const uint32_t knrec = (uint32_t)(((int64_t)(S - 1) * krow + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, knrec);
   const uint16_t* vbase = (const uint16_t*)a.v + b * a.vs0 + head * a.vs2;
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2));
+  const uint32_t vnrec = (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, vnrec);
 
-  // per-thread staging coordinates (fixed for the whole loop)
-  int k_key[KCH], k_dch[KCH], k_off[KCH], k_lds[KCH];
+  // direct-load lane roles: run j of this wave covers LDS bytes
+  // [(wave*RUNS + j) * 1024, +1024); lane L fills 16 bytes at 16*L of it
+  int k_row[RUNS], k_src[RUNS], v_row[RUNS], v_src[RUNS];
 #pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int ci = tid + i * NT;
-    k_key[i] = ci / DCH;
-    int dch = ci % DCH;
-    if constexpr (KFUSED) dch = (dch >> 1) + (dch & 1) * (DCH / 2);  // pair partner = lane ^ 1
-    k_dch[i] = dch;
-    k_off[i] = (int)((k_key[i] * krow + dch * 8) * 2);
-    k_lds[i] = key_lds_row(k_key[i]) * KP + dch * 8;
+  for (int j = 0; j < RUNS; ++j) {
+    const int run = wave * RUNS + j;
+    const int rr = run * RPR + lane / CPR;  // LDS row
+    const int pos = lane % CPR;             // physical chunk in the row
+    k_row[j] = key_of_row(rr);
+    k_src[j] = (int)((k_row[j] * krow + (pos ^ (rr & 7)) * 8) * 2);
+    v_row[j] = rr;
+    v_src[j] = (int)(((int64_t)rr * a.vs1 + (pos ^ ((rr & 3) << 1)) * 8) * 2);
   }
-  const int vkg = tid % VKG, vdc = tid / VKG;
-  const int v_off = (int)(((int64_t)vkg * VKR * a.vs1 + vdc * 8) * 2);
-  const int v_rowb = (int)(a.vs1 * 2);
-  const int v_lds = (vdc * 8) * VP + vkg * VKR;
 
-  u32x4 kr[KCH], vr[VKR];
-  float2 csr[KFUSED ? KCH : 1][4];
-
-  auto load_tile = [&](int t) {
-    const int n0 = t * BN;
-    const int ks = (int)(n0 * krow * 2);
+  // fused mode stages raw K through registers: chunk roles per thread
+  int fk_key[KFUSED ? KCH : 1], fk_c[KFUSED ? KCH : 1];
+  u32x4 fkr[KFUSED ? KCH : 1];
+  float2 fcs[KFUSED ? KCH : 1][4];
+  if constexpr (KFUSED) {
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
-      kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_off[i], ks, 0);
-      if constexpr (KFUSED) {
-        const int n = min(n0 + k_key[i], S - 1);
-        const int j0 = (k_dch[i] % (DCH / 2)) * 8 + (k_dch[i] >= DCH / 2 ? 4 : 0);
-        const float2* cp = a.cs + ((int64_t)b * S + n) * (D / 2) + j0;
-        // lanes dch and dch^1 share one group of 8 pair angles: each fetches
-        // 4 and the halves are swapped at store time
+      const int ci = tid + i * NT;
+      fk_key[i] = ci / CPR;
+      const int raw = ci % CPR;
+      fk_c[i] = (raw >> 1) + (raw & 1) * (CPR / 2);  // rotary partner chunk sits in lane ^ 1
+    }
+  }
+
+  auto issue_k = [&](int t, int buf) {
+    const int n0 = t * BN;
+    if constexpr (!KFUSED) {
+      const bool msk = tile_masked(n0);
+      const int nb = n0 * (int)(krow * 2);
+      char* dst = Ksm + buf * TILEB;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) csr[i][e] = cp[e];
+      for (int j = 0; j < RUNS; ++j) {
+        uint32_t off = (uint32_t)(k_src[j] + nb);
+        if (msk) off = key_ok(n0 + k_row[j]) ? off : knrec;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_ptr_t)(dst + (wave * RUNS + j) * 1024), 16,
+                                                 off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int n = n0 + fk_key[i];
+        const uint32_t off = key_ok(n) ? (uint32_t)((n * krow + fk_c[i] * 8) * 2) : knrec;
+        fkr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+        const int j0 = (fk_c[i] % (CPR / 2)) * 8 + (fk_c[i] >= CPR / 2 ? 4 : 0);
+        const float2* cp = a.cs + ((int64_t)b * S + min(n, S - 1)) * (D / 2) + j0;
+        // lanes c and c^1 share one group of 8 pair angles: each fetches 4
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fcs[i][e] = cp[e];
       }
     }
-    const int vs = n0 * v_rowb;
-#pragma unroll
-    for (int i = 0; i < VKR; ++i)
-      vr[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, v_off + i * v_rowb, vs, 0);
   };
 
-  auto store_tile = [&](int t, int buf) {
-    const int n0 = t * BN;
-    uint16_t* kd = Ks + buf * KBUF;
-    uint16_t* vd = Vt + buf * VBUF;
+  // fused mode: RMSNorm + M-RoPE of the staged raw K rows, written as K'
+  auto finish_k = [&](int buf) {
+    if constexpr (KFUSED) {
+      char* dst = Ksm + buf * TILEB;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      u32x4 w = kr[i];
-      if constexpr (KFUSED) {
-        // RMSNorm over the lanes holding this key row, then rotate pairs
-        // (the lane holding chunk c < DCH/2 has x1, its neighbour lane^1 x2).
+      for (int i = 0; i < KCH; ++i) {
+        const u32x4 w = fkr[i];
         float x[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { x[2 * e] = bf16_lo(w[e]); x[2 * e + 1] = bf16_hi(w[e]); }
@@ -229,59 +259,68 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
-        for (int s = 1; s < DCH; s <<= 1) ss += __shfl_xor(ss, s, DCH);
+        for (int s = 1; s < CPR; s <<= 1) ss += __shfl_xor(ss, s, CPR);
         const float r = rsqrtf(ss * (1.0f / D) + a.eps);
-        const int dch = k_dch[i];
-        const bool first = dch < DCH / 2;
+        const int c = fk_c[i];
+        const bool first = c < CPR / 2;
         float y[8], px[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * a.gk[dch * 8 + e];
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * a.gk[c * 8 + e];
 #pragma unroll
         for (int e = 0; e < 8; ++e) px[e] = __shfl_xor(y[e], 1, 64);
         float2 cs8[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 mine = csr[i][e];
+          const float2 mine = fcs[i][e];
           const float2 other = make_float2(__shfl_xor(mine.x, 1, 64), __shfl_xor(mine.y, 1, 64));
           cs8[e] = first ? mine : other;
           cs8[4 + e] = first ? other : mine;
         }
+        u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float c = cs8[e].x, s = cs8[e].y;
-          y[e] = first ? (y[e] * c - px[e] * s) : (y[e] * c + px[e] * s);
+        for (int e = 0; e < 4; ++e) {
+          float z[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int q = 2 * e + h;
+            z[h] = first ? (y[q] * cs8[q].x - px[q] * cs8[q].y) : (y[q] * cs8[q].x + px[q] * cs8[q].y);
+          }
+          o[e] = pack_bf16(z[0], z[1]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
-      }
-      *(u32x4*)&kd[k_lds[i]] = w;
-    }
-    // V rows of padded text keys (and rows past the end) become zeros so a
-    // non-finite value there cannot reach P.V (their P is exactly 0).
-    if (n0 + BN > S || (n0 + BN > L && n0 < T)) {
-#pragma unroll
-      for (int i = 0; i < VKR; ++i) {
-        const int n = n0 + vkg * VKR + i;
-        if (n >= S || (n >= L && n < T)) vr[i] = u32x4{0u, 0u, 0u, 0u};
+        // LDS row holding key fk_key: inverse of key_of_row within its 32-block
+        const int kk = fk_key[i], w5 = kk & 31;
+        const int rr = (kk & ~31) | (((w5 >> 2) & 3) << 3) | ((w5 >> 4) << 2) | (w5 & 3);
+        *(u32x4*)(dst + k_lds_off<D>(rr, c)) = o;
       }
     }
-    // VKR keys x 8 dims -> 8 rows of V^T, VKR keys each
+  };
+
+  auto issue_v = [&](int t, int buf) {
+    const int n0 = t * BN;
+    const bool msk = tile_masked(n0);
+    const int nb = n0 * (int)(a.vs1 * 2);
+    char* dst = Vsm + buf * TILEB;
 #pragma unroll
-    for (int d2 = 0; d2 < 4; ++d2) {
-      uint32_t lo[VKR / 2], hi[VKR / 2];
+    for (int j = 0; j < RUNS; ++j) {
+      // V rows of padded keys read as zeros, so non-finite values there
+      // cannot reach P.V (their probability is exactly 0)
+      uint32_t off = (uint32_t)(v_src[j] + nb);
+      if (msk) off = key_ok(n0 + v_row[j]) ? off : vnrec;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_ptr_t)(dst + (wave * RUNS + j) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+
+  // S^T (log2 units, relative to the running max) of one tile
+  auto qk = [&](int buf, float minus_m, f32x16* st) {
+    const char* src = Ksm + buf * TILEB;
 #pragma unroll
-      for (int i = 0; i < VKR; i += 2) {
-        lo[i / 2] = __builtin_amdgcn_perm(vr[i + 1][d2], vr[i][d2], 0x05040100u);
-        hi[i / 2] = __builtin_amdgcn_perm(vr[i + 1][d2], vr[i][d2], 0x07060302u);
-      }
-      uint16_t* r0 = vd + v_lds + 2 * d2 * VP;
-      uint16_t* r1 = r0 + VP;
-      if constexpr (VKR == 4) {
-        *(u32x2*)r0 = u32x2{lo[0], lo[1]};
-        *(u32x2*)r1 = u32x2{hi[0], hi[1]};
-      } else {
-        *(uint32_t*)r0 = lo[0];
-        *(uint32_t*)r1 = hi[0];
+    for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kb][i] = minus_m;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const bf16x8 av = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
+        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], st[kb], 0, 0, 0);
       }
     }
   };
@@ -291,94 +330,153 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float mrun = -INFINITY, lrun = 0.f;
-  const float c2 = a.c2;
+  float mrun = 0.f, lrun = 0.f;
+
+  // v-operand read roles (transposing LDS read): lane 16g + j of a 16-lane
+  // group addresses key (g/2)*16 + j/4 (+ u*8 + half*4 + kb*32) and head_dim
+  // 16*(g%2) + 4*(j%4) (+ db*32); lane l then holds 4 consecutive keys of
+  // dim db*32 + l%32.
+  const int vg = lane >> 4, vj = lane & 15;
+  const int v_key0 = (vg >> 1) * 16 + (vj >> 2);
+  const int v_dim0 = 16 * (vg & 1) + 4 * (vj & 3);
 
   int t = 0;
   while (t < ntiles && skipped(t)) ++t;
-  int buf = 0;
+  int t1 = t < ntiles ? next_tile(t) : ntiles;
+  int cur = 0;
+  // S^T of the current tile and of the next one live in separate register
+  // sets (sa / sb swap roles every tile), so the next tile's Q.K' can run on
+  // the matrix cores while the current tile's exponentials are computed
+  f32x16 sa[NB], sb[NB];
   if (t < ntiles) {
-    load_tile(t);
-    store_tile(t, 0);
+    issue_v(t, 0);
+    issue_k(t, 0);
+    if constexpr (KFUSED) {
+      finish_k(0);
+    } else {
+      if (t1 < ntiles) issue_k(t1, 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    qk(0, -mrun, sa);
   }
-  __syncthreads();
+  bool first = true;
+  float lrun2 = 0.f;  // second partial row sum (two chains for latency)
 
-  while (t < ntiles) {
-    const int tn = next_tile(t);
-    if (tn < ntiles) load_tile(tn);
-
-    const int n0 = t * BN;
-    const uint16_t* kc = Ks + buf * KBUF;
-    const uint16_t* vc = Vt + buf * VBUF;
-    // S^T = K' Q'^T for each 32-key block
-    f32x16 st[NB];
-#pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st[kb][i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x8 av = *(const bf16x8*)&kc[(kb * 32 + m) * KP + c * 16 + hf * 8];
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], st[kb], 0, 0, 0);
+  // one tile: st holds S^T(t) on entry; S^T(t1) is produced into sn
+  auto step = [&](f32x16* st, f32x16* sn) {
+    const int t2 = t1 < ntiles ? next_tile(t1) : ntiles;
+    // K'(t1) and V(t) are in LDS and every wave is done with K'(t) and V(t-1)
+    if constexpr (KFUSED) {
+      if (t1 < ntiles) {
+        issue_k(t1, cur ^ 1);
+        finish_k(cur ^ 1);
       }
     }
-    // key-padding / sequence-end mask (select, so NaN in masked keys cannot leak)
-    if (n0 + BN > S || (n0 + BN > L && n0 < T)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if constexpr (!KFUSED) {
+      if (t2 < ntiles) issue_k(t2, cur);
+    }
+    if (t1 < ntiles) issue_v(t1, cur ^ 1);
+
+    const int n0 = t * BN;
+    if (tile_masked(n0)) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int n = n0 + kb * 32 + hf * 16 + i;
-          const bool ok = n < S && !(n >= L && n < T);
-          st[kb][i] = ok ? st[kb][i] : -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          st[kb][i] = key_ok(n0 + kb * 32 + hf * 16 + i) ? st[kb][i] : -INFINITY;
     }
-    // online softmax in the log2 domain, lazily rescaled
+    // row max of this tile relative to the running max
     float mx = st[0][0];
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][i]);
-    mx = half_swap_max(mx) * c2;
-    if (__builtin_amdgcn_ballot_w64(mx > mrun + kRescaleLog2) != 0) {
-      const float mnew = fmaxf(mrun, mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-      mrun = mnew;
-      lrun *= alpha;
+    mx = half_swap_max(mx);
+    if (first || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2) != 0) {
+      const float delta = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      mrun += delta;
+      lrun = first ? 0.f : lrun * alpha;
+      lrun2 = first ? 0.f : lrun2 * alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= first ? 0.f : alpha;
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[kb][i] -= delta;
+      first = false;
     }
+
+    // exponentials (P rounded to bf16) and the row sum of the rounded P,
+    // interleaved with Q.K'(t1) on the matrix cores
     bf16x8 pf[NB][2];
+    auto exps = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][u * 8 + e], c2, -mrun));
+          for (int e = 0; e < 8; ++e) pf[kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(st[kb][u * 8 + e]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pp = {pf[kb][u][e], pf[kb][u][e + 1]};
-          lrun = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lrun, false);
+          for (int e = 0; e < 8; e += 4) {
+            const bf16x2 p0 = {pf[kb][u][e], pf[kb][u][e + 1]};
+            const bf16x2 p1 = {pf[kb][u][e + 2], pf[kb][u][e + 3]};
+            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+            lrun = __builtin_amdgcn_fdot2_f32_bf16(p0, one, lrun, false);
+            lrun2 = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lrun2, false);
+          }
         }
-      }
-    // O^T += V^T P^T
+    };
+    // (after the last tile this Q.K' reads the idle buffer; its result is
+    // never used, and keeping it unconditional keeps the block branch-free)
+    qk(cur ^ 1, -mrun, sn);
+    exps();
+#pragma unroll
+    for (int i = 0; i < NB * KC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU (incl. transcendental)
+    }
+
+    // O^T += V^T P^T. The wave raises its issue priority for this matrix-core
+    // run so the SIMD's other wave (in its exponential phase) fills around it.
+    __builtin_amdgcn_s_setprio(1);
+    const char* vsrc = Vsm + cur * TILEB;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 av = *(const bf16x8*)&vc[(db * 32 + m) * VP + kb * 32 + hf * 16 + u * 8];
+          const int key = kb * 32 + u * 8 + v_key0;
+          const int dim = db * 32 + v_dim0;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vsrc + v_lds_off<D>(key, dim >> 3) + (dim & 7) * 2));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vsrc + v_lds_off<D>(key + 4, dim >> 3) + (dim & 7) * 2));
+          // assemble the operand from whole dwords: building it from 16-bit
+          // elements is miscompiled by this toolchain (halves get duplicated)
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[kb][u], oacc[db], 0, 0, 0);
         }
-    if (tn < ntiles) store_tile(tn, buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
+    __builtin_amdgcn_s_setprio(0);
+    cur ^= 1;
+    t = t1;
+    t1 = t2;
+  };
+
+  while (t < ntiles) {
+    step(sa, sb);
+    if (t >= ntiles) break;
+    step(sb, sa);
   }
+  lrun += lrun2;
 
   // ---- epilogue: O / l, padded rows are exact zeros (selected, not scaled,
   // so whatever a padded query row computed cannot leak)

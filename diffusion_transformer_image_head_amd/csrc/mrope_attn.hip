@@ -5,7 +5,7 @@
 #include <cstdlib>
 #include <cstring>
 
-#include "../../include/mrope_attn.h"
+#include "mrope_attn.h"
 #include "attn_bf16.hpp"
 #include "attn_fp32.hpp"
 #include "prologue.hpp"
