@@ -10,14 +10,17 @@
 // zero output rows).
 //
 // Work decomposition: one workgroup per (batch, head, BM-row query tile),
-// WAVES waves of 32 query rows each. Per wave, everything is held "transposed"
-// so a query row lives in one lane pair (lanes m and m + 32):
+// WAVES waves of RB x 32 query rows each. Per wave, everything is held
+// "transposed" so a query row lives in one lane pair (lanes m and m + 32):
 //   S^T (keys x queries) = K' Q'^T   v_mfma_f32_32x32x16_bf16, A = K' from LDS,
 //                                    B = Q' from registers;
 //   O^T (dims x queries) += V^T P^T  same MFMA, A = V^T read from LDS with the
 //                                    gfx950 transposing LDS read, B = P taken
 //                                    straight from the S^T accumulators.
-// Row max / row sum are lane-local plus one permlane32 swap.
+// Row max / row sum are lane-local plus one permlane32 swap. With RB = 2 a
+// wave owns two 32-row blocks, so every K'/V fragment read from LDS feeds two
+// MFMAs (half the LDS traffic per FLOP of RB = 1); it then needs ~380
+// registers and runs one wave per SIMD.
 //
 // LDS: K' and V tiles arrive by buffer loads that write LDS directly (lane L of
 // a load lands at 16*L of a 1 KiB run), with 16-byte chunks XOR-swizzled per
@@ -53,6 +56,11 @@ __device__ __forceinline__ int key_of_row(int r) {
   return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
 }
 
+template <int N>
+struct Parity {
+  static constexpr int value = N;
+};
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
@@ -64,9 +72,9 @@ __device__ __forceinline__ int k_lds_off(int r, int c) { return r * (D * 2) + ((
 template <int D>
 __device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4); }
 
-template <int D, int WAVES, int BN, bool KFUSED>
-__global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
-  constexpr int BM = WAVES * 32;
+template <int D, int WAVES, int BN, int RB, bool KFUSED>
+__global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Args a) {
+  constexpr int BM = WAVES * 32 * RB;
   constexpr int NT = WAVES * 64;
   constexpr int KC = D / 16;                 // 16-wide head_dim chunks (QK^T k-steps)
   constexpr int DB = D / 32;                 // 32-row blocks of O^T
@@ -80,8 +88,14 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   static_assert(RUNS >= 1 && RUNS * WAVES * 1024 == TILEB, "tile must split into whole runs");
   static_assert(KCH >= 1 && KCH * NT == BN * CPR, "fused staging must cover the tile");
 
-  __shared__ __attribute__((aligned(1024))) char Ksm[2 * TILEB];
-  __shared__ __attribute__((aligned(1024))) char Vsm[2 * TILEB];
+  // Four separate LDS objects (not one indexed array): the buffer parity is a
+  // compile-time constant in each unrolled step, so the compiler can see that
+  // a step's direct loads and its LDS reads touch different objects and does
+  // not make the reads wait for the loads just issued.
+  __shared__ __attribute__((aligned(1024))) char K0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char K1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char V1[TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
@@ -91,23 +105,32 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   const int S = a.S, T = a.T;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
   const int q0 = qt * BM;
-  const int row = q0 + wave * 32 + m;
-  const bool in_seq = row < S;
-  const bool valid_row = in_seq && !(row >= L && row < T);
-
-  uint16_t* outp = (uint16_t*)a.out + b * a.os0 + (int64_t)row * a.os1 + head * a.os2;
-  float* lsep = a.lse ? a.lse + ((int64_t)b * a.H + head) * S + row : nullptr;
+  int row[RB];
+  bool in_seq[RB], valid_row[RB];
+  uint16_t* outp[RB];
+  float* lsep[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    row[rb] = q0 + (wave * RB + rb) * 32 + m;
+    in_seq[rb] = row[rb] < S;
+    valid_row[rb] = in_seq[rb] && !(row[rb] >= L && row[rb] < T);
+    outp[rb] = (uint16_t*)a.out + b * a.os0 + (int64_t)row[rb] * a.os1 + head * a.os2;
+    lsep[rb] = a.lse ? a.lse + ((int64_t)b * a.H + head) * S + row[rb] : nullptr;
+  }
 
   // Query tile made only of padded text slots: zeros, no attention.
   const int q_end = min(q0 + BM, S);
   if (q0 >= L && q_end <= T) {
-    if (in_seq) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+      if (in_seq[rb]) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(u32x2*)(outp + db * 32 + g * 8 + hf * 4) = u32x2{0u, 0u};
-      if (lsep && hf == 0) *lsep = -INFINITY;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *(u32x2*)(outp[rb] + db * 32 + g * 8 + hf * 4) = u32x2{0u, 0u};
+        if (lsep[rb] && hf == 0) *lsep[rb] = -INFINITY;
+      }
     }
     return;
   }
@@ -115,11 +138,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   // ---- Q prologue: RMSNorm + M-RoPE in fp32, scaled by softmax_scale*log2(e),
   // one bf16 rounding, kept as the B operand of S^T: lane (m, hf) holds
   // Q'[row][c*16 + hf*8 + e].
-  bf16x8 qf[KC];
-  {
+  bf16x8 qf[RB][KC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     float x[KC][8];
-    if (in_seq) {
-      const uint16_t* src = (const uint16_t*)a.q + b * a.qs0 + (int64_t)row * a.qs1 + head * a.qs2;
+    if (in_seq[rb]) {
+      const uint16_t* src = (const uint16_t*)a.q + b * a.qs0 + (int64_t)row[rb] * a.qs1 + head * a.qs2;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const u32x4 w = *(const u32x4*)(src + c * 16 + hf * 8);
@@ -144,7 +168,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     const float r = rsqrtf(ss * (1.0f / D) + a.eps);
     const float c2 = a.c2;
     // (cos, sin) of this token's pairs from the table the prologue pass wrote
-    const float2* csrow = a.cs + ((int64_t)b * S + min(row, S - 1)) * (D / 2);
+    const float2* csrow = a.cs + ((int64_t)b * S + min(row[rb], S - 1)) * (D / 2);
 #pragma unroll
     for (int c = 0; c < KC / 2; ++c) {
       const f32x4 g1a = *(const f32x4*)(a.gq + c * 16 + hf * 8);
@@ -161,8 +185,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
         const float cs = t4[e >> 1][(e & 1) * 2], sn = t4[e >> 1][(e & 1) * 2 + 1];
         const float u = x[c][e] * r * g1;
         const float w = x[c + KC / 2][e] * r * g2;
-        qf[c][e] = (__bf16)((u * cs - w * sn) * c2);
-        qf[c + KC / 2][e] = (__bf16)((w * cs + u * sn) * c2);
+        qf[rb][c][e] = (__bf16)((u * cs - w * sn) * c2);
+        qf[rb][c + KC / 2][e] = (__bf16)((w * cs + u * sn) * c2);
       }
     }
   }
@@ -222,7 +246,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     if constexpr (!KFUSED) {
       const bool msk = tile_masked(n0);
       const int nb = n0 * (int)(krow * 2);
-      char* dst = Ksm + buf * TILEB;
+      char* dst = buf ? K1 : K0;
 #pragma unroll
       for (int j = 0; j < RUNS; ++j) {
         uint32_t off = (uint32_t)(k_src[j] + nb);
@@ -248,7 +272,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
   // fused mode: RMSNorm + M-RoPE of the staged raw K rows, written as K'
   auto finish_k = [&](int buf) {
     if constexpr (KFUSED) {
-      char* dst = Ksm + buf * TILEB;
+      char* dst = buf ? K1 : K0;
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
         const u32x4 w = fkr[i];
@@ -299,7 +323,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     const int n0 = t * BN;
     const bool msk = tile_masked(n0);
     const int nb = n0 * (int)(a.vs1 * 2);
-    char* dst = Vsm + buf * TILEB;
+    char* dst = buf ? V1 : V0;
 #pragma unroll
     for (int j = 0; j < RUNS; ++j) {
       // V rows of padded keys read as zeros, so non-finite values there
@@ -310,27 +334,22 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
     }
   };
 
-  // S^T (log2 units, relative to the running max) of one tile
-  auto qk = [&](int buf, float minus_m, f32x16* st) {
-    const char* src = Ksm + buf * TILEB;
+  f32x16 oacc[RB][DB];
+  float mrun[RB], lrun[RB], lrun2[RB], neg_m[RB];
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb) {
+  for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st[kb][i] = minus_m;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        const bf16x8 av = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], st[kb], 0, 0, 0);
-      }
-    }
+      for (int i = 0; i < 16; ++i) oacc[rb][db][i] = 0.f;
+    mrun[rb] = 0.f;
+    lrun[rb] = 0.f;
+    lrun2[rb] = 0.f;  // second partial row sum (two chains for latency)
+  }
+  auto refresh_neg_m = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) neg_m[rb] = -mrun[rb];
   };
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float mrun = 0.f, lrun = 0.f;
 
   // v-operand read roles (transposing LDS read): lane 16g + j of a 16-lane
   // group addresses key (g/2)*16 + j/4 (+ u*8 + half*4 + kb*32) and head_dim
@@ -342,111 +361,134 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
 
   int t = 0;
   while (t < ntiles && skipped(t)) ++t;
-  int t1 = t < ntiles ? next_tile(t) : ntiles;
-  int cur = 0;
-  // S^T of the current tile and of the next one live in separate register
-  // sets (sa / sb swap roles every tile), so the next tile's Q.K' can run on
-  // the matrix cores while the current tile's exponentials are computed
-  f32x16 sa[NB], sb[NB];
+  refresh_neg_m();
   if (t < ntiles) {
     issue_v(t, 0);
     issue_k(t, 0);
-    if constexpr (KFUSED) {
-      finish_k(0);
-    } else {
-      if (t1 < ntiles) issue_k(t1, 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    qk(0, -mrun, sa);
+    if constexpr (KFUSED) finish_k(0);
   }
   bool first = true;
-  float lrun2 = 0.f;  // second partial row sum (two chains for latency)
 
-  // one tile: st holds S^T(t) on entry; S^T(t1) is produced into sn
-  auto step = [&](f32x16* st, f32x16* sn) {
-    const int t2 = t1 < ntiles ? next_tile(t1) : ntiles;
-    // K'(t1) and V(t) are in LDS and every wave is done with K'(t) and V(t-1)
-    if constexpr (KFUSED) {
-      if (t1 < ntiles) {
-        issue_k(t1, cur ^ 1);
-        finish_k(cur ^ 1);
-      }
-    }
+  // one tile t whose K' and V were loaded into buffer `parity`; the loads of
+  // the next tile go to the other buffer while this one is computed
+  auto step = [&](auto parity) {
+    constexpr int cur = decltype(parity)::value;
+    const int tn = next_tile(t);
+    // K'(t) and V(t) are in LDS and every wave is done with buffer cur ^ 1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if constexpr (!KFUSED) {
-      if (t2 < ntiles) issue_k(t2, cur);
+    if (tn < ntiles) {
+      issue_v(tn, cur ^ 1);
+      issue_k(tn, cur ^ 1);
+      if constexpr (KFUSED) finish_k(cur ^ 1);
     }
-    if (t1 < ntiles) issue_v(t1, cur ^ 1);
+
+    // S^T = K'(t) Q'^T - m: all K' fragments of the tile are read first so
+    // the reads overlap each other and the MFMAs that consume them
+    f32x16 st[RB][NB];
+    {
+      const char* src = cur ? K1 : K0;
+      bf16x8 kf[KC][NB];
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+          kf[c][kb] = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[rb][kb][i] = neg_m[rb];
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c], st[rb][kb], 0, 0, 0);
+      // keep kAhead fragment reads in flight ahead of the MFMAs
+      constexpr int kFrags = KC * NB, kAhead = kFrags / 2;
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+      for (int i = 0; i < kFrags; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+        if (i + kAhead < kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
 
     const int n0 = t * BN;
     if (tile_masked(n0)) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          st[kb][i] = key_ok(n0 + kb * 32 + hf * 16 + i) ? st[kb][i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const bool ok = key_ok(n0 + kb * 32 + hf * 16 + i);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) st[rb][kb][i] = ok ? st[rb][kb][i] : -INFINITY;
+        }
     }
     // row max of this tile relative to the running max
-    float mx = st[0][0];
+    float mx[RB];
+    bool grow = false;
 #pragma unroll
-    for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][i]);
-    mx = half_swap_max(mx);
-    if (first || __builtin_amdgcn_ballot_w64(mx > kRescaleLog2) != 0) {
-      const float delta = first ? mx : fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      mrun += delta;
-      lrun = first ? 0.f : lrun * alpha;
-      lrun2 = first ? 0.f : lrun2 * alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= first ? 0.f : alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      float v = st[rb][0][0];
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[kb][i] -= delta;
+        for (int i = 0; i < 16; ++i) v = fmaxf(v, st[rb][kb][i]);
+      mx[rb] = half_swap_max(v);
+      grow = grow || mx[rb] > kRescaleLog2;
+    }
+    if (first || __builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float delta = first ? mx[rb] : fmaxf(mx[rb], 0.f);
+        const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(-delta);
+        mrun[rb] += delta;
+        lrun[rb] *= alpha;
+        lrun2[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[rb][db][i] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) st[rb][kb][i] -= delta;
+      }
       first = false;
+      refresh_neg_m();
     }
 
-    // exponentials (P rounded to bf16) and the row sum of the rounded P,
-    // interleaved with Q.K'(t1) on the matrix cores
-    bf16x8 pf[NB][2];
-    auto exps = [&]() {
+    // exponentials (P rounded to bf16) and the row sum of the rounded P
+    bf16x8 pf[RB][NB][2];
+    {
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pf[kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(st[kb][u * 8 + e]);
+          for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int e = 0; e < 8; e += 4) {
-            const bf16x2 p0 = {pf[kb][u][e], pf[kb][u][e + 1]};
-            const bf16x2 p1 = {pf[kb][u][e + 2], pf[kb][u][e + 3]};
-            const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-            lrun = __builtin_amdgcn_fdot2_f32_bf16(p0, one, lrun, false);
-            lrun2 = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lrun2, false);
+            for (int e = 0; e < 8; ++e)
+              pf[rb][kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(st[rb][kb][u * 8 + e]);
+#pragma unroll
+            for (int e = 0; e < 8; e += 4) {
+              const bf16x2 p0 = {pf[rb][kb][u][e], pf[rb][kb][u][e + 1]};
+              const bf16x2 p1 = {pf[rb][kb][u][e + 2], pf[rb][kb][u][e + 3]};
+              lrun[rb] = __builtin_amdgcn_fdot2_f32_bf16(p0, one, lrun[rb], false);
+              lrun2[rb] = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lrun2[rb], false);
+            }
           }
-        }
-    };
-    // (after the last tile this Q.K' reads the idle buffer; its result is
-    // never used, and keeping it unconditional keeps the block branch-free)
-    qk(cur ^ 1, -mrun, sn);
-    exps();
-#pragma unroll
-    for (int i = 0; i < NB * KC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);  // four VALU (incl. transcendental)
     }
 
     // O^T += V^T P^T. The wave raises its issue priority for this matrix-core
     // run so the SIMD's other wave (in its exponential phase) fills around it.
     __builtin_amdgcn_s_setprio(1);
-    const char* vsrc = Vsm + cur * TILEB;
+    const char* vsrc = cur ? V1 : V0;
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -463,37 +505,39 @@ __global__ __launch_bounds__(WAVES * 64, 2) void attn_bf16_kernel(Args a) {
           // elements is miscompiled by this toolchain (halves get duplicated)
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
           const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[kb][u], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[rb][kb][u], oacc[rb][db], 0, 0, 0);
         }
     __builtin_amdgcn_s_setprio(0);
-    cur ^= 1;
-    t = t1;
-    t1 = t2;
+    t = tn;
   };
 
   while (t < ntiles) {
-    step(sa, sb);
+    step(Parity<0>{});
     if (t >= ntiles) break;
-    step(sb, sa);
+    step(Parity<1>{});
   }
-  lrun += lrun2;
 
   // ---- epilogue: O / l, padded rows are exact zeros (selected, not scaled,
   // so whatever a padded query row computed cannot leak)
-  const float ltot = half_swap_sum(lrun);
-  if (!in_seq) return;
-  const float inv = 1.0f / ltot;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float ltot = half_swap_sum(lrun[rb] + lrun2[rb]);
+    if (!in_seq[rb]) continue;
+    const float inv = 1.0f / ltot;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t w0 = pack_bf16(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
-      uint32_t w1 = pack_bf16(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
-      w0 = valid_row ? w0 : 0u;
-      w1 = valid_row ? w1 : 0u;
-      *(u32x2*)(outp + db * 32 + g * 8 + hf * 4) = u32x2{w0, w1};
-    }
-  if (lsep && hf == 0) *lsep = valid_row ? mrun * kLn2 + logf(ltot) : -INFINITY;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t w0 = pack_bf16(oacc[rb][db][g * 4 + 0] * inv, oacc[rb][db][g * 4 + 1] * inv);
+        uint32_t w1 = pack_bf16(oacc[rb][db][g * 4 + 2] * inv, oacc[rb][db][g * 4 + 3] * inv);
+        w0 = valid_row[rb] ? w0 : 0u;
+        w1 = valid_row[rb] ? w1 : 0u;
+        *(u32x2*)(outp[rb] + db * 32 + g * 8 + hf * 4) = u32x2{w0, w1};
+      }
+    if (lsep[rb] && hf == 0) *lsep[rb] = valid_row[rb] ? mrun[rb] * kLn2 + logf(ltot) : -INFINITY;
+  }
 }
 
 }  // namespace mra

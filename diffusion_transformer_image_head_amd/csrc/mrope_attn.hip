@@ -15,8 +15,15 @@ namespace {
 using mra::Args;
 
 constexpr int kWaves = 4;
-constexpr int kBlockN = 64;
-constexpr int kBlockM = kWaves * 32;
+#ifndef MRA_BLOCK_N
+#define MRA_BLOCK_N 64
+#endif
+constexpr int kBlockN = MRA_BLOCK_N;  // keys per K/V tile
+#ifndef MRA_ROW_BLOCKS
+#define MRA_ROW_BLOCKS 1
+#endif
+constexpr int kRowBlocks = MRA_ROW_BLOCKS;  // 32-row blocks per wave
+constexpr int kBlockM = kWaves * 32 * kRowBlocks;
 constexpr int kFp32BlockM = 64;
 constexpr size_t kWsAlign = 256;
 
@@ -110,9 +117,9 @@ hipError_t launch_attend_bf16(Args& a, int kpro, hipStream_t s) {
   a.n_qt = (a.S + kBlockM - 1) / kBlockM;
   a.grid = a.B * a.H * a.n_qt;
   if (kpro == MRA_KPRO_PREPASS)
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, false>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, false>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, true>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, true>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
