@@ -43,15 +43,36 @@ def kernel_source_hash() -> str:
 
 def traffic_from_profile(config: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, when it was taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"attn_bf16_{config}_hbm_traffic.json")
+    summary (``key: value`` lines), when it was taken on the current kernel
+    sources; else None."""
+    path = os.path.join(PROFILES, f"attn_bf16_{config}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
+    rec = {}
     with open(path) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(nbytes: int = 256 << 20, reps: int = 5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) of the attention kernel."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_per_copy": nbytes, "copies": reps}), flush=True)
 
 
 def cpu_baseline(w, gpu_out):
@@ -84,7 +105,12 @@ def main():
     ap.add_argument("--config", default="1024px", choices=["512px", "1024px", "ragged", "long"])
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(heads/batch shard with no exchange; see the design notes)", file=sys.stderr)
