@@ -3,14 +3,14 @@
 on one MI355X.
 
 One step = one full pass of the path over one batch: the prologue pass
-(rotary table + K') and the attention kernel, i.e. one ``mrope_attn_fwd``
-call, on inputs already resident in HBM. Default workload: the 1024px shape
+(rotary table + K') and the attend stage (the attention kernel, plus the
+small merge kernel of the query tiles split across key ranges), i.e. one
+``mrope_attn_fwd`` call, on inputs already resident in HBM. Default workload: the 1024px shape
 (B=1, H=32, head_dim=128, 512 text + 64x64 image tokens = 4608 tokens).
 
 Prints one JSON line. ``value`` is algorithmic TFLOP/s of the whole step
-(4*H*D*sum_b n_b^2 over real tokens), ``roofline`` the attention kernel's
-own rate (HIP events around that kernel on its stream) against the bf16
-dense MFMA peak, and ``cpu_baseline`` the fp64 oracle timed on the host on
+(4*H*D*sum_b n_b^2 over real tokens), ``roofline`` the attend stage's own
+rate (HIP events around it on its stream) against the bf16 dense MFMA peak, and ``cpu_baseline`` the fp64 oracle timed on the host on
 the same workload (with the GPU output checked against it).
 """
 
@@ -42,7 +42,7 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profile(config: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
+    """HBM bytes per attend stage from the committed rocprofv3 counter
     summary (``key: value`` lines), when it was taken on the current kernel
     sources; else None."""
     path = os.path.join(PROFILES, f"attn_bf16_{config}_hbm_traffic.txt")
@@ -175,7 +175,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(args.config),
-                     "kernel_ms": round(attn_ms, 5), "kernel": "attn_bf16_kernel"},
+                     "kernel_ms": round(attn_ms, 5), "kernel": "attn_bf16_kernel + split_merge_kernel"},
         "frac_of_peak_whole_step": round(value / PEAK_BF16_TFLOPS, 4),
         "wall_s": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),

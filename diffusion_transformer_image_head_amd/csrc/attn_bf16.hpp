@@ -72,6 +72,17 @@ __device__ __forceinline__ int k_lds_off(int r, int c) { return r * (D * 2) + ((
 template <int D>
 __device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4); }
 
+// Split query tiles: part p of split tile st stores, for each 32-row block rr
+// of the tile, one record of 64 * (D/2 + 2) floats: the unnormalised O^T
+// accumulators as [D/8 chunks][64 lanes][4] (chunk db*4 + g of lane (m, hf)
+// holds dims db*32 + g*8 + hf*4 .. +3 of query row rr*32 + m), then the running
+// max (log2 units) and the row sum, [64 lanes] each.
+template <int D, int WAVES, int RB>
+__device__ __forceinline__ float* part_record(const Args& a, int st, int p, int rr) {
+  constexpr int REC = 64 * (D / 2 + 2);
+  return a.part + (((int64_t)st * a.nsplit + p) * (WAVES * RB) + rr) * REC;
+}
+
 template <int D, int WAVES, int BN, int RB, bool KFUSED>
 __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Args a) {
   constexpr int BM = WAVES * 32 * RB;
@@ -99,8 +110,18 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
-  const int bid = xcd_remap(blockIdx.x, a.grid);
-  const int qt = bid % a.n_qt, bh = bid / a.n_qt;
+  // workgroup -> (tile, key-range part): whole tiles first (XCD-aware order),
+  // then nsplit parts of each of the last n_split tiles
+  int tile, part = 0, nparts = 1;
+  if ((int)blockIdx.x < a.n_whole) {
+    tile = xcd_remap(blockIdx.x, a.n_whole);
+  } else {
+    const int s_ = blockIdx.x - a.n_whole;
+    tile = a.n_whole + s_ / a.nsplit;
+    part = s_ % a.nsplit;
+    nparts = a.nsplit;
+  }
+  const int qt = tile % a.n_qt, bh = tile / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
   const int S = a.S, T = a.T;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
@@ -191,8 +212,11 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     }
   }
 
-  // ---- tile bookkeeping: tiles with no valid key are skipped
-  const int ntiles = (S + BN - 1) / BN;
+  // ---- tile bookkeeping: this workgroup covers key tiles [t_lo, ntiles);
+  // tiles with no valid key are skipped
+  const int ktiles = (S + BN - 1) / BN;
+  const int t_lo = (int)((int64_t)part * ktiles / nparts);
+  const int ntiles = (int)((int64_t)(part + 1) * ktiles / nparts);
   auto skipped = [&](int t) { const int n0 = t * BN; return n0 >= L && min(n0 + BN, S) <= T; };
   auto next_tile = [&](int t) {
     ++t;
@@ -359,7 +383,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   const int v_key0 = (vg >> 1) * 16 + (vj >> 2);
   const int v_dim0 = 16 * (vg & 1) + 4 * (vj & 3);
 
-  int t = 0;
+  int t = t_lo;
   while (t < ntiles && skipped(t)) ++t;
   refresh_neg_m();
   if (t < ntiles) {
@@ -519,13 +543,36 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     step(Parity<1>{});
   }
 
+  // ---- row sums (both lane halves hold a share of each row)
+  float ltot[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) ltot[rb] = half_swap_sum(lrun[rb] + lrun2[rb]);
+
+  // ---- split tile: this part's unnormalised (O, m, l) go to the workspace;
+  // split_merge_kernel combines the parts after this launch
+  if (nparts > 1) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float* rec = part_record<D, WAVES, RB>(a, tile - a.n_whole, part, wave * RB + rb);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(rec + ((db * 4 + g) * 64 + lane) * 4) =
+              f32x4{oacc[rb][db][g * 4], oacc[rb][db][g * 4 + 1], oacc[rb][db][g * 4 + 2], oacc[rb][db][g * 4 + 3]};
+      // a part that processed no key tile contributes nothing
+      rec[DB * 16 * 64 + lane] = first ? -INFINITY : mrun[rb];
+      rec[DB * 16 * 64 + 64 + lane] = ltot[rb];
+    }
+    return;
+  }
+
   // ---- epilogue: O / l, padded rows are exact zeros (selected, not scaled,
   // so whatever a padded query row computed cannot leak)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const float ltot = half_swap_sum(lrun[rb] + lrun2[rb]);
     if (!in_seq[rb]) continue;
-    const float inv = 1.0f / ltot;
+    const float inv = 1.0f / ltot[rb];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -536,8 +583,73 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
         w1 = valid_row[rb] ? w1 : 0u;
         *(u32x2*)(outp[rb] + db * 32 + g * 8 + hf * 4) = u32x2{w0, w1};
       }
-    if (lsep[rb] && hf == 0) *lsep[rb] = valid_row[rb] ? mrun[rb] * kLn2 + logf(ltot) : -INFINITY;
+    if (lsep[rb] && hf == 0) *lsep[rb] = valid_row[rb] ? mrun[rb] * kLn2 + logf(ltot[rb]) : -INFINITY;
   }
+}
+
+// Combines the nsplit parts of each split query tile by the log-sum-exp rule
+// and writes the output rows and LSE exactly as the attention epilogue does.
+// One thread per (split tile, 32-row block, 4-dim chunk, lane).
+template <int D, int WAVES, int RB>
+__global__ __launch_bounds__(256) void split_merge_kernel(Args a) {
+  constexpr int BM = WAVES * 32 * RB;
+  constexpr int CH = D / 8;  // 4-float chunks per lane record
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int lane = gid & 63, m = lane & 31, hf = lane >> 5;
+  const int c = (gid >> 6) % CH;
+  const int rr = (gid >> 6) / CH % (WAVES * RB);
+  const int st = (gid >> 6) / CH / (WAVES * RB);
+  if (st >= a.n_split) return;
+  const int tile = a.n_whole + st;
+  const int qt = tile % a.n_qt, bh = tile / a.n_qt;
+  const int head = bh % a.H, b = bh / a.H;
+  const int S = a.S, T = a.T;
+  const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
+  const int q0 = qt * BM;
+  // a tile made only of padded text slots was written by the attention kernel
+  if (q0 >= L && min(q0 + BM, S) <= T) return;
+  const int row = q0 + rr * 32 + m;
+  if (row >= S) return;
+  const bool valid_row = !(row >= L && row < T);
+  const int nparts = a.nsplit;
+
+  // every part's loads are issued before any is used
+  float mp[kMaxSplit], lp[kMaxSplit];
+  f32x4 op[kMaxSplit];
+#pragma unroll
+  for (int p = 0; p < kMaxSplit; ++p) {
+    if (p < nparts) {
+      const float* rec = part_record<D, WAVES, RB>(a, st, p, rr);
+      mp[p] = rec[CH * 4 * 64 + lane];
+      lp[p] = rec[CH * 4 * 64 + 64 + lane];
+      op[p] = *(const f32x4*)(rec + (c * 64 + lane) * 4);
+    }
+  }
+  float m_all = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < kMaxSplit; ++p)
+    if (p < nparts) m_all = fmaxf(m_all, mp[p]);
+  float l_all = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < kMaxSplit; ++p) {
+    if (p < nparts) {
+      const float f = mp[p] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp[p] - m_all);
+      l_all += f * lp[p];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += f * op[p][e];
+    }
+  }
+  const float inv = 1.0f / l_all;
+  uint32_t w0 = pack_bf16(o[0] * inv, o[1] * inv);
+  uint32_t w1 = pack_bf16(o[2] * inv, o[3] * inv);
+  w0 = valid_row ? w0 : 0u;
+  w1 = valid_row ? w1 : 0u;
+  const int db = c >> 2, g = c & 3;
+  uint16_t* outp = (uint16_t*)a.out + b * a.os0 + (int64_t)row * a.os1 + head * a.os2;
+  *(u32x2*)(outp + db * 32 + g * 8 + hf * 4) = u32x2{w0, w1};
+  if (a.lse && c == 0 && hf == 0)
+    a.lse[((int64_t)b * a.H + head) * S + row] = valid_row ? m_all * kLn2 + logf(l_all) : -INFINITY;
 }
 
 }  // namespace mra

@@ -18,6 +18,7 @@ namespace mra {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxHalf = 64;  // head_dim <= 128
+constexpr int kMaxSplit = 8;  // key-range parts per split query tile
 
 // Rotary frequencies theta^(-2j/D), rounded once to fp32 on the host, and the
 // section boundaries: pair j follows t if j < sec_t, h if j < sec_th, else w.
@@ -46,6 +47,13 @@ struct Args {
   int32_t B, S, H, T;
   int32_t n_qt;             // query tiles per (batch, head)
   int32_t grid;             // workgroups launched
+  // Tiles [0, n_whole) are computed by one workgroup each; the remaining
+  // n_split tiles by nsplit workgroups each over disjoint key ranges, whose
+  // partial (O, max, sum) go to `part` and are merged by a second launch.
+  int32_t n_whole;
+  int32_t n_split;
+  int32_t nsplit;
+  float* part;
   float eps;
   float c2;                 // softmax scale * log2(e)
   float scale;

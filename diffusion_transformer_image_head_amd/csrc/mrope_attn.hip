@@ -1,6 +1,7 @@
 // C ABI of libmrope_attn.so: argument validation, workspace sizing, kernel
 // selection and launch on the caller's stream. The operation and the
 // conventions are documented in include/mrope_attn.h.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -26,6 +27,16 @@ constexpr int kRowBlocks = MRA_ROW_BLOCKS;  // 32-row blocks per wave
 constexpr int kBlockM = kWaves * 32 * kRowBlocks;
 constexpr int kFp32BlockM = 64;
 constexpr size_t kWsAlign = 256;
+// Attention workgroups resident at once on an MI355X (256 CUs, two per CU).
+constexpr int kComputeUnits = 256;
+constexpr int kResidentSlots = kComputeUnits * (kRowBlocks == 1 ? 2 : 1);
+// Workgroups the split tiles of the last wave are spread over: one per CU
+// (measured faster than filling both slots of every CU, which doubles the
+// partial results the merge pass reads).
+#ifndef MRA_SPLIT_TARGET
+#define MRA_SPLIT_TARGET kComputeUnits
+#endif
+constexpr int kSplitTarget = MRA_SPLIT_TARGET;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -65,18 +76,50 @@ int check_strides(const int64_t* st, int dtype) {
   return MRA_OK;
 }
 
-// Workspace layout (bf16 path): the (cos, sin) table [B, S, D/2] float2 at
-// offset 0, then, for the prepass K prologue, K' [B, H, S, D] bf16.
+// How the bf16 attention grid is laid out. When the last round of whole
+// query tiles would leave most resident slots idle, the last n_split tiles are
+// cut into nsplit key ranges each, computed by separate workgroups and merged.
+struct Plan {
+  int n_qt, tiles, n_whole, n_split, nsplit;
+  size_t part_floats;  // per split workgroup
+};
+
+Plan make_plan(const mra_desc* d) {
+  Plan p;
+  p.n_qt = (d->seq + kBlockM - 1) / kBlockM;
+  p.tiles = d->batch * d->heads * p.n_qt;
+  const int ktiles = (d->seq + kBlockN - 1) / kBlockN;
+  int r = p.tiles >= kResidentSlots ? p.tiles % kResidentSlots : p.tiles;
+  int k = 1;
+  // split only when the last wave would leave at least half of the compute
+  // units idle (a unit running one workgroup instead of two is not idle)
+  if (r > 0 && 4 * r <= kResidentSlots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
+  if (k < 2) { r = 0; k = 1; }
+  p.n_split = r;
+  p.nsplit = k;
+  p.n_whole = p.tiles - r;
+  p.part_floats = (size_t)kRowBlocks * kWaves * 64 * (d->head_dim / 32 * 16 + 2);
+  return p;
+}
+
+// Workspace layout (bf16 path), each piece 256-byte aligned: the (cos, sin)
+// table [B, S, D/2] float2; K' [B, H, S, D] bf16 (prepass K prologue only);
+// split-tile partial records (fp32).
 size_t table_bytes(const mra_desc* d) {
   return round_up((size_t)d->batch * d->seq * (d->head_dim / 2) * sizeof(float2), kWsAlign);
+}
+size_t kprime_bytes(const mra_desc* d) {
+  if (resolve_kprologue(d) != MRA_KPRO_PREPASS) return 0;
+  return round_up((size_t)d->batch * d->seq * d->heads * d->head_dim * sizeof(uint16_t), kWsAlign);
+}
+size_t part_bytes(const mra_desc* d) {
+  const Plan p = make_plan(d);
+  return round_up((size_t)p.n_split * p.nsplit * p.part_floats * sizeof(float), kWsAlign);
 }
 
 size_t workspace_bytes(const mra_desc* d) {
   if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0) return 0;
-  size_t n = table_bytes(d);
-  if (resolve_kprologue(d) == MRA_KPRO_PREPASS)
-    n += round_up((size_t)d->batch * d->seq * d->heads * d->head_dim * sizeof(uint16_t), kWsAlign);
-  return n;
+  return table_bytes(d) + kprime_bytes(d) + part_bytes(d);
 }
 
 void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const void* v,
@@ -114,12 +157,14 @@ hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
 
 template <int D>
 hipError_t launch_attend_bf16(Args& a, int kpro, hipStream_t s) {
-  a.n_qt = (a.S + kBlockM - 1) / kBlockM;
-  a.grid = a.B * a.H * a.n_qt;
   if (kpro == MRA_KPRO_PREPASS)
     hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, false>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
   else
     hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, true>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+  if (a.n_split) {
+    const int64_t threads = (int64_t)a.n_split * kWaves * kRowBlocks * (D / 8) * 64;
+    hipLaunchKernelGGL((mra::split_merge_kernel<D, kWaves, kRowBlocks>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -202,8 +247,18 @@ static int prepare_call(const mra_desc* d, const void* q, const void* k, const v
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
   fill_args(a, d, q, k, v, pos, gq, gk, seq_lens, out, lse);
   if (d->dtype == MRA_BF16) {
-    a.cs = (float2*)workspace;
-    if (resolve_kprologue(d) == MRA_KPRO_PREPASS) a.kp = (uint16_t*)((char*)workspace + table_bytes(d));
+    char* w = (char*)workspace;
+    a.cs = (float2*)w;
+    w += table_bytes(d);
+    if (resolve_kprologue(d) == MRA_KPRO_PREPASS) a.kp = (uint16_t*)w;
+    w += kprime_bytes(d);
+    const Plan p = make_plan(d);
+    a.n_qt = p.n_qt;
+    a.n_whole = p.n_whole;
+    a.n_split = p.n_split;
+    a.nsplit = p.nsplit;
+    a.grid = p.n_whole + p.n_split * p.nsplit;
+    a.part = p.n_split ? (float*)w : nullptr;
   }
   return MRA_OK;
 }

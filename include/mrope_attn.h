@@ -113,7 +113,10 @@ size_t mrope_attn_workspace_size(const mra_desc* desc);
 
 /* The fused forward pass (see the top of this file). workspace must hold at
  * least mrope_attn_workspace_size(desc) bytes (16-byte aligned) when that
- * size is nonzero; it is scratch, overwritten by the call. out must not
+ * size is nonzero; it is scratch, overwritten by the call (for bf16 it holds
+ * the rotary table, K' with MRA_KPRO_PREPASS, and the fp32 partial results of
+ * the query tiles that would otherwise run in a last, mostly idle wave of
+ * workgroups: those are cut into key ranges and merged by a second kernel). out must not
  * overlap q, k, v or the workspace. Launches on `stream` and returns without
  * synchronising. */
 int mrope_attn_fwd(const mra_desc* desc, const void* q, const void* k, const void* v,

@@ -136,9 +136,16 @@ def test_workspace_sizes(lib):
     d = desc(batch=1, seq=4608, heads=32, text_pad=512)
     table = 4608 * 64 * 8
     kprime = 4608 * 32 * 128 * 2
-    assert B.workspace_size(d) == table + kprime                   # auto = prepass
+    # 1152 query tiles of 128 rows over 512 resident workgroups leave 128 for
+    # the last wave, each cut into 2 key ranges (one workgroup per CU): a
+    # (O[64], m, l) fp32 record per lane of 256 lanes per part
+    split = 128 * 2 * 256 * (128 // 2 + 2) * 4
+    assert B.workspace_size(d) == table + kprime + split           # auto = prepass
     assert B.workspace_size(desc(batch=1, seq=4608, heads=32, text_pad=512,
-                                 kprologue="fused")) == table
+                                 kprologue="fused")) == table + split
+    # 1024 tiles fill two waves exactly: nothing is split
+    assert B.workspace_size(desc(batch=1, seq=4096, heads=32, text_pad=512,
+                                 kprologue="fused")) == 4096 * 64 * 8
     assert B.workspace_size(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
     assert B.workspace_size(desc(section=(1, 2, 3))) == 0          # invalid -> 0
     assert lib.mrope_attn_workspace_size(None) == 0
