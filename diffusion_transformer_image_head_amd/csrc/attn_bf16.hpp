@@ -65,12 +65,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
 
+// LDS swizzles. The gfx950 LDS has 64 four-byte banks (256 bytes per bank
+// row) and serves a 128-bit read for 16 lanes, a 64-bit read for 32 lanes, per
+// clock. Logical 16-byte chunk c of tile row r sits at physical chunk
+// c ^ swz(r) (XOR: the map is its own inverse, so the direct loads use it to
+// pick the source chunk of each LDS slot). With RPB tile rows per bank row:
+// - K' (128-bit reads, 16 lanes = 16 consecutive rows, same chunk): the rows
+//   that share banks get distinct chunks, swz = (r / RPB) mod chunks-per-row;
+// - V (transposing 64-bit reads, 32 lanes = 4 consecutive keys x 4 chunks):
+//   the 4 keys get disjoint 4-chunk groups, swz = 4 * ((r / RPB) mod (4 / RPB)).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  constexpr int RPB = 256 / (D * 2), CPR = D / 8;
+  return (r / RPB) & (CPR - 1);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  constexpr int RPB = 256 / (D * 2);
+  return ((r / RPB) & (4 / RPB - 1)) << 2;
+}
 // Byte offset inside a swizzled LDS tile of logical 16-byte chunk c of row r.
-// K' tiles XOR the chunk with (r & 7); V tiles with 2 * (r & 3).
 template <int D>
-__device__ __forceinline__ int k_lds_off(int r, int c) { return r * (D * 2) + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ int k_lds_off(int r, int c) { return r * (D * 2) + ((c ^ k_swz<D>(r)) << 4); }
 template <int D>
-__device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4); }
+__device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((c ^ v_swz<D>(r)) << 4); }
 
 // Split query tiles: part p of split tile st stores, for each 32-row block rr
 // of the tile, one record of 64 * (D/2 + 2) floats: the unnormalised O^T
@@ -246,9 +264,9 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     const int rr = run * RPR + lane / CPR;  // LDS row
     const int pos = lane % CPR;             // physical chunk in the row
     k_row[j] = key_of_row(rr);
-    k_src[j] = (int)((k_row[j] * krow + (pos ^ (rr & 7)) * 8) * 2);
+    k_src[j] = (int)((k_row[j] * krow + (pos ^ k_swz<D>(rr)) * 8) * 2);
     v_row[j] = rr;
-    v_src[j] = (int)(((int64_t)rr * a.vs1 + (pos ^ ((rr & 3) << 1)) * 8) * 2);
+    v_src[j] = (int)(((int64_t)rr * a.vs1 + (pos ^ v_swz<D>(rr)) * 8) * 2);
   }
 
   // fused mode stages raw K through registers: chunk roles per thread
