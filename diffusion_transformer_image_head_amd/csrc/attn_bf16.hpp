@@ -45,6 +45,7 @@
 namespace mra {
 
 constexpr float kRescaleLog2 = 8.0f;
+
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource, 32-bit data format
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -125,6 +126,8 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char K1[TILEB];
   __shared__ __attribute__((aligned(1024))) char V0[TILEB];
   __shared__ __attribute__((aligned(1024))) char V1[TILEB];
+  auto kbuf = [&](int i) -> char* { return i ? K1 : K0; };
+  auto vbuf = [&](int i) -> char* { return i ? V1 : V0; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     if constexpr (!KFUSED) {
       const bool msk = tile_masked(n0);
       const int nb = n0 * (int)(krow * 2);
-      char* dst = buf ? K1 : K0;
+      char* dst = kbuf(buf);
 #pragma unroll
       for (int j = 0; j < RUNS; ++j) {
         uint32_t off = (uint32_t)(k_src[j] + nb);
@@ -314,7 +317,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   // fused mode: RMSNorm + M-RoPE of the staged raw K rows, written as K'
   auto finish_k = [&](int buf) {
     if constexpr (KFUSED) {
-      char* dst = buf ? K1 : K0;
+      char* dst = kbuf(buf);
 #pragma unroll
       for (int i = 0; i < KCH; ++i) {
         const u32x4 w = fkr[i];
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     const int n0 = t * BN;
     const bool msk = tile_masked(n0);
     const int nb = n0 * (int)(a.vs1 * 2);
-    char* dst = buf ? V1 : V0;
+    char* dst = vbuf(buf);
 #pragma unroll
     for (int j = 0; j < RUNS; ++j) {
       // V rows of padded keys read as zeros, so non-finite values there
@@ -404,62 +407,45 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   int t = t_lo;
   while (t < ntiles && skipped(t)) ++t;
   refresh_neg_m();
-  if (t < ntiles) {
-    issue_v(t, 0);
-    issue_k(t, 0);
-    if constexpr (KFUSED) finish_k(0);
-  }
   bool first = true;
 
-  // one tile t whose K' and V were loaded into buffer `parity`; the loads of
-  // the next tile go to the other buffer while this one is computed
-  auto step = [&](auto parity) {
-    constexpr int cur = decltype(parity)::value;
-    const int tn = next_tile(t);
-    // K'(t) and V(t) are in LDS and every wave is done with buffer cur ^ 1
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tn < ntiles) {
-      issue_v(tn, cur ^ 1);
-      issue_k(tn, cur ^ 1);
-      if constexpr (KFUSED) finish_k(cur ^ 1);
+  // S^T = K'(t) Q'^T - m from K' buffer `kpar`: all K' fragments of the tile
+  // are read first so the reads overlap each other and the MFMAs using them
+  auto qk = [&](auto kpar, f32x16 (&st)[RB][NB]) {
+    constexpr int cur = decltype(kpar)::value;
+    const char* src = kbuf(cur);
+    bf16x8 kf[KC][NB];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+        kf[c][kb] = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[rb][kb][i] = neg_m[rb];
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+#pragma unroll
+      for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c], st[rb][kb], 0, 0, 0);
+    // keep kAhead fragment reads in flight ahead of the MFMAs
+    constexpr int kFrags = KC * NB, kAhead = kFrags / 2;
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+    for (int i = 0; i < kFrags; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+      if (i + kAhead < kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+  };
 
-    // S^T = K'(t) Q'^T - m: all K' fragments of the tile are read first so
-    // the reads overlap each other and the MFMAs that consume them
-    f32x16 st[RB][NB];
-    {
-      const char* src = cur ? K1 : K0;
-      bf16x8 kf[KC][NB];
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-          kf[c][kb] = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) st[rb][kb][i] = neg_m[rb];
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-#pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c], st[rb][kb], 0, 0, 0);
-      // keep kAhead fragment reads in flight ahead of the MFMAs
-      constexpr int kFrags = KC * NB, kAhead = kFrags / 2;
-      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-      for (int i = 0; i < kFrags; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
-        if (i + kAhead < kFrags) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-
-    const int n0 = t * BN;
+  // masking, running max (lazy rescale of O and the row sums), exponentials
+  // rounded to bf16 as the P operand, and the row sum of the rounded P
+  auto softmax = [&](f32x16 (&st)[RB][NB], int n0, bf16x8 (&pf)[RB][NB][2]) {
     if (tile_masked(n0)) {
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
@@ -503,34 +489,29 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
       first = false;
       refresh_neg_m();
     }
-
-    // exponentials (P rounded to bf16) and the row sum of the rounded P
-    bf16x8 pf[RB][NB][2];
-    {
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int kb = 0; kb < NB; ++kb)
+      for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              pf[rb][kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(st[rb][kb][u * 8 + e]);
+          for (int e = 0; e < 8; ++e) pf[rb][kb][u][e] = (__bf16)__builtin_amdgcn_exp2f(st[rb][kb][u * 8 + e]);
 #pragma unroll
-            for (int e = 0; e < 8; e += 4) {
-              const bf16x2 p0 = {pf[rb][kb][u][e], pf[rb][kb][u][e + 1]};
-              const bf16x2 p1 = {pf[rb][kb][u][e + 2], pf[rb][kb][u][e + 3]};
-              lrun[rb] = __builtin_amdgcn_fdot2_f32_bf16(p0, one, lrun[rb], false);
-              lrun2[rb] = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lrun2[rb], false);
-            }
+          for (int e = 0; e < 8; e += 4) {
+            const bf16x2 p0 = {pf[rb][kb][u][e], pf[rb][kb][u][e + 1]};
+            const bf16x2 p1 = {pf[rb][kb][u][e + 2], pf[rb][kb][u][e + 3]};
+            lrun[rb] = __builtin_amdgcn_fdot2_f32_bf16(p0, one, lrun[rb], false);
+            lrun2[rb] = __builtin_amdgcn_fdot2_f32_bf16(p1, one, lrun2[rb], false);
           }
-    }
+        }
+  };
 
-    // O^T += V^T P^T. The wave raises its issue priority for this matrix-core
-    // run so the SIMD's other wave (in its exponential phase) fills around it.
-    __builtin_amdgcn_s_setprio(1);
-    const char* vsrc = cur ? V1 : V0;
+  // O^T += V^T P^T from V buffer `vpar`
+  auto pv = [&](auto vpar, const bf16x8 (&pf)[RB][NB][2]) {
+    constexpr int cur = decltype(vpar)::value;
+    const char* vsrc = vbuf(cur);
 #pragma unroll
     for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
@@ -551,10 +532,37 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
           for (int rb = 0; rb < RB; ++rb)
             oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[rb][kb][u], oacc[rb][db], 0, 0, 0);
         }
+  };
+
+  if (t < ntiles) {
+    issue_v(t, 0);
+    issue_k(t, 0);
+    if constexpr (KFUSED) finish_k(0);
+  }
+  // one tile t whose K' and V were loaded into buffer `parity`; the loads
+  // of the next tile go to the other buffer while this one is computed
+  auto step = [&](auto parity) {
+    constexpr int cur = decltype(parity)::value;
+    const int tn = next_tile(t);
+    // K'(t) and V(t) are in LDS and every wave is done with buffer cur ^ 1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tn < ntiles) {
+      issue_v(tn, cur ^ 1);
+      issue_k(tn, cur ^ 1);
+      if constexpr (KFUSED) finish_k(cur ^ 1);
+    }
+    f32x16 st[RB][NB];
+    qk(parity, st);
+    bf16x8 pf[RB][NB][2];
+    softmax(st, t * BN, pf);
+    // The wave raises its issue priority for this matrix-core run so the
+    // SIMD's other wave (in its exponential phase) fills around it.
+    __builtin_amdgcn_s_setprio(1);
+    pv(parity, pf);
     __builtin_amdgcn_s_setprio(0);
     t = tn;
   };
-
   while (t < ntiles) {
     step(Parity<0>{});
     if (t >= ntiles) break;
