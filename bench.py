@@ -97,12 +97,85 @@ def cpu_baseline(w, gpu_out):
     }, {"max_abs": float(np.abs(d).max()), "rel_rms": rel}
 
 
+def bench_cfg(args):
+    """One guided sampling step at 1024px: the conditional pass (512 text slots
+    + 64x64 image) and the unconditional pass (the 4096 image tokens alone)
+    as one grouped call, against the same two problems as two plain calls."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_attn_group
+    from diffusion_transformer_image_head_amd.workloads import config_workload, make_workload
+
+    lib()
+    cond = config_workload("1024px")
+    unc = make_workload(1, 32, 128, (16, 24, 24), 0, 64, 64, dtype="bf16", seed=21)
+    unc.pos = np.ascontiguousarray(cond.pos[:, cond.text_pad:])
+    dev = torch.device("cuda:0")
+    probs = []
+    for w in (cond, unc):
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+        probs.append(dict(q=t(w.q).to(torch.bfloat16), k=t(w.k).to(torch.bfloat16),
+                          v=t(w.v).to(torch.bfloat16), pos=t(w.pos), gamma_q=t(w.gamma_q),
+                          gamma_k=t(w.gamma_k), text_pad=w.text_pad, section=w.section))
+    for p in probs:
+        p["out"] = torch.empty_like(p["q"])
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
+
+    def grouped():
+        mrope_attn_group(probs, workspace=ws)
+
+    def separate():
+        for p, w in zip(probs, (ws, ws2)):
+            mrope_attn(p["q"], p["k"], p["v"], p["pos"], p["gamma_q"], p["gamma_k"],
+                       text_pad=p["text_pad"], section=p["section"], out=p["out"], workspace=w)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_sep = timed(separate)
+    ms = timed(grouped)
+    flops = cond.flops() + unc.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC + " (guided step: cond + uncond)", "value": round(value, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights)",
+        "config": {"workload": "cfg1024: 1024px cond (B=1 H=32 D=128, 512 text + 64x64 image) "
+                               "+ image-only uncond (4096 tokens), one grouped call"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "whole grouped call (prologues + attention + merge)"},
+        "separate_calls": {"ms_per_step": round(ms_sep, 5),
+                           "value": round(flops / (ms_sep * 1e-3) / 1e12, 3)},
+    }
+    if not args.no_cpu_baseline:
+        base, par = cpu_baseline(cond, probs[0]["out"].float().cpu().numpy().astype(np.float64))
+        rec["cpu_baseline"] = dict(base, sample="the conditional pass only (" + base["sample"] + ")")
+        rec["parity"] = par
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="1024px", choices=["512px", "1024px", "ragged", "long"])
+    ap.add_argument("--config", default="1024px",
+                    choices=["512px", "1024px", "ragged", "long", "cfg1024"],
+                    help="cfg1024: one guided step, the 1024px conditional pass and its "
+                         "image-only unconditional pass in one grouped call")
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -115,6 +188,10 @@ def main():
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(heads/batch shard with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+
+    if args.config == "cfg1024":
+        bench_cfg(args)
+        return
 
     import numpy as np
     import torch

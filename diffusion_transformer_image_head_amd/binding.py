@@ -33,6 +33,15 @@ class Desc(ctypes.Structure):
     ]
 
 
+class Problem(ctypes.Structure):
+    """Mirror of ``mra_problem`` (include/mrope_attn.h)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k", "v", "pos_thw", "gamma_q", "gamma_k", "seq_lens", "out", "lse")]
+
+
+MAX_GROUP = 4
+
+
 class MraError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"mrope_attn status {status}: {msg}")
@@ -65,6 +74,11 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_attend.restype = ctypes.c_int
         L.mrope_attn_status_string.argtypes = [ctypes.c_int]
         L.mrope_attn_status_string.restype = ctypes.c_char_p
+        L.mrope_attn_group_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int]
+        L.mrope_attn_group_workspace_size.restype = ctypes.c_size_t
+        L.mrope_attn_fwd_group.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Problem), ctypes.c_int,
+                                           vp, ctypes.c_size_t, vp]
+        L.mrope_attn_fwd_group.restype = ctypes.c_int
         L.mrope_attn_abi_version.argtypes = []
         L.mrope_attn_abi_version.restype = ctypes.c_int
         _lib = L
@@ -108,18 +122,9 @@ def _bsd_strides(t):
     return (t.stride(0), t.stride(1), t.stride(2))
 
 
-def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
-               section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
-               return_lse: bool = False, kprologue="auto", out=None, workspace=None,
-               stage: str = "fwd"):
-    """Fused QK-RMSNorm + 3D M-RoPE joint attention on the current HIP stream.
-
-    q, k, v: [B, S, H, D] bf16 or fp32 GPU tensors (head_dim contiguous; any
-    batch/token/head strides, e.g. views of one fused qkv buffer).
-    pos: [B, S, 3] int32 (t, h, w). gamma_q, gamma_k: [D] fp32.
-    seq_lens: [B] int32 true text lengths (<= text_pad) or None.
-    Returns out [B, S, H, D] (q's dtype), and lse [B, H, S] fp32 if asked.
-    """
+def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_pad, section,
+             theta, eps, scale, kprologue):
+    """Shape/dtype/device checks; returns (desc, out, lse, seq_lens)."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("pos", pos), ("gamma_q", gamma_q),
@@ -152,6 +157,26 @@ def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     desc = make_desc(b, s, h, d, text_pad=text_pad, section=section, theta=theta, eps=eps,
                      scale=scale, dtype=dt, kprologue=kprologue, q_stride=_bsd_strides(q),
                      k_stride=_bsd_strides(k), v_stride=_bsd_strides(v), o_stride=_bsd_strides(out))
+    return desc, out, lse, seq_lens
+
+
+def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
+               section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
+               return_lse: bool = False, kprologue="auto", out=None, workspace=None,
+               stage: str = "fwd"):
+    """Fused QK-RMSNorm + 3D M-RoPE joint attention on the current HIP stream.
+
+    q, k, v: [B, S, H, D] bf16 or fp32 GPU tensors (head_dim contiguous; any
+    batch/token/head strides, e.g. views of one fused qkv buffer).
+    pos: [B, S, 3] int32 (t, h, w). gamma_q, gamma_k: [D] fp32.
+    seq_lens: [B] int32 true text lengths (<= text_pad) or None.
+    Returns out [B, S, H, D] (q's dtype), and lse [B, H, S] fp32 if asked.
+    """
+    import torch
+
+    desc, out, lse, seq_lens = _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse,
+                                        text_pad=text_pad, section=section, theta=theta, eps=eps,
+                                        scale=scale, kprologue=kprologue)
     need = workspace_size(desc)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -194,3 +219,47 @@ def prepared_call(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, **kw):
         return mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens, stage="attend", **common)
 
     return prepare, attend, out
+
+
+def group_workspace_size(descs) -> int:
+    arr = (Desc * len(descs))(*descs)
+    return int(lib().mrope_attn_group_workspace_size(arr, len(descs)))
+
+
+def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", workspace=None):
+    """Several attention problems in one attention launch (e.g. the
+    conditional [text + image] and unconditional [image only] passes of one
+    guided sampling step). ``problems`` is a list of dicts with the arguments
+    of :func:`mrope_attn`: q, k, v, pos, gamma_q, gamma_k, and optionally
+    seq_lens, text_pad (default 0), section, theta, eps, scale, out.
+    Returns the list of outputs (of (out, lse) pairs if ``return_lse``)."""
+    import torch
+
+    if not 1 <= len(problems) <= MAX_GROUP:
+        raise ValueError(f"1..{MAX_GROUP} problems per group")
+    descs, probs, results = [], [], []
+    for p in problems:
+        desc, out, lse, sl = _checked(
+            p["q"], p["k"], p["v"], p["pos"], p["gamma_q"], p["gamma_k"], p.get("seq_lens"),
+            p.get("out"), return_lse, text_pad=p.get("text_pad", 0),
+            section=p.get("section", (16, 24, 24)), theta=p.get("theta", 10000.0),
+            eps=p.get("eps", 1e-6), scale=p.get("scale"), kprologue=kprologue)
+        descs.append(desc)
+        probs.append(Problem(p["q"].data_ptr(), p["k"].data_ptr(), p["v"].data_ptr(),
+                             p["pos"].data_ptr(), p["gamma_q"].data_ptr(), p["gamma_k"].data_ptr(),
+                             None if sl is None else sl.data_ptr(), out.data_ptr(),
+                             None if lse is None else lse.data_ptr()))
+        results.append((out, lse) if return_lse else out)
+    n = len(descs)
+    darr = (Desc * n)(*descs)
+    parr = (Problem * n)(*probs)
+    need = int(lib().mrope_attn_group_workspace_size(darr, n))
+    dev = problems[0]["q"].device
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().mrope_attn_fwd_group(darr, parr, n, None if not need else workspace.data_ptr(),
+                                    need, stream)
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return results

@@ -97,13 +97,13 @@ __device__ __forceinline__ int v_lds_off(int r, int c) { return r * (D * 2) + ((
 // holds dims db*32 + g*8 + hf*4 .. +3 of query row rr*32 + m), then the running
 // max (log2 units) and the row sum, [64 lanes] each.
 template <int D, int WAVES, int RB>
-__device__ __forceinline__ float* part_record(const Args& a, int st, int p, int rr) {
+__device__ __forceinline__ float* part_record(float* part, int nsplit, int st, int p, int rr) {
   constexpr int REC = 64 * (D / 2 + 2);
-  return a.part + (((int64_t)st * a.nsplit + p) * (WAVES * RB) + rr) * REC;
+  return part + (((int64_t)st * nsplit + p) * (WAVES * RB) + rr) * REC;
 }
 
-template <int D, int WAVES, int BN, int RB, bool KFUSED>
-__global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Args a) {
+template <int D, int WAVES, int BN, int RB, bool KFUSED, int G>
+__global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Group<G> gp) {
   constexpr int BM = WAVES * 32 * RB;
   constexpr int NT = WAVES * 64;
   constexpr int KC = D / 16;                 // 16-wide head_dim chunks (QK^T k-steps)
@@ -131,17 +131,19 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 31, hf = lane >> 5;
-  // workgroup -> (tile, key-range part): whole tiles first (XCD-aware order),
-  // then nsplit parts of each of the last n_split tiles
-  int tile, part = 0, nparts = 1;
-  if ((int)blockIdx.x < a.n_whole) {
-    tile = xcd_remap(blockIdx.x, a.n_whole);
+  // workgroup -> (global tile, key-range part): whole tiles first (XCD-aware
+  // order), then nsplit parts of each of the last n_split tiles
+  int gt, part = 0, nparts = 1;
+  if ((int)blockIdx.x < gp.n_whole) {
+    gt = xcd_remap(blockIdx.x, gp.n_whole);
   } else {
-    const int s_ = blockIdx.x - a.n_whole;
-    tile = a.n_whole + s_ / a.nsplit;
-    part = s_ % a.nsplit;
-    nparts = a.nsplit;
+    const int s_ = blockIdx.x - gp.n_whole;
+    gt = gp.n_whole + s_ / gp.nsplit;
+    part = s_ % gp.nsplit;
+    nparts = gp.nsplit;
   }
+  int tile;
+  const Args& a = gp.p[group_problem(gp, gt, tile)];
   const int qt = tile % a.n_qt, bh = tile / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
   const int S = a.S, T = a.T;
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   if (nparts > 1) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float* rec = part_record<D, WAVES, RB>(a, tile - a.n_whole, part, wave * RB + rb);
+      float* rec = part_record<D, WAVES, RB>(gp.part, nparts, gt - gp.n_whole, part, wave * RB + rb);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -616,8 +618,8 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
 // Combines the nsplit parts of each split query tile by the log-sum-exp rule
 // and writes the output rows and LSE exactly as the attention epilogue does.
 // One thread per (split tile, 32-row block, 4-dim chunk, lane).
-template <int D, int WAVES, int RB>
-__global__ __launch_bounds__(256) void split_merge_kernel(Args a) {
+template <int D, int WAVES, int RB, int G>
+__global__ __launch_bounds__(256) void split_merge_kernel(Group<G> gp) {
   constexpr int BM = WAVES * 32 * RB;
   constexpr int CH = D / 8;  // 4-float chunks per lane record
   const int gid = blockIdx.x * 256 + threadIdx.x;
@@ -625,8 +627,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(Args a) {
   const int c = (gid >> 6) % CH;
   const int rr = (gid >> 6) / CH % (WAVES * RB);
   const int st = (gid >> 6) / CH / (WAVES * RB);
-  if (st >= a.n_split) return;
-  const int tile = a.n_whole + st;
+  if (st >= gp.n_split) return;
+  int tile;
+  const Args& a = gp.p[group_problem(gp, gp.n_whole + st, tile)];
   const int qt = tile % a.n_qt, bh = tile / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
   const int S = a.S, T = a.T;
@@ -637,7 +640,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(Args a) {
   const int row = q0 + rr * 32 + m;
   if (row >= S) return;
   const bool valid_row = !(row >= L && row < T);
-  const int nparts = a.nsplit;
+  const int nparts = gp.nsplit;
 
   // every part's loads are issued before any is used
   float mp[kMaxSplit], lp[kMaxSplit];
@@ -645,7 +648,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(Args a) {
 #pragma unroll
   for (int p = 0; p < kMaxSplit; ++p) {
     if (p < nparts) {
-      const float* rec = part_record<D, WAVES, RB>(a, st, p, rr);
+      const float* rec = part_record<D, WAVES, RB>(gp.part, nparts, st, p, rr);
       mp[p] = rec[CH * 4 * 64 + lane];
       lp[p] = rec[CH * 4 * 64 + 64 + lane];
       op[p] = *(const f32x4*)(rec + (c * 64 + lane) * 4);

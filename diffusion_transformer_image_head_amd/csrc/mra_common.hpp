@@ -46,19 +46,38 @@ struct Args {
   int64_t os0, os1, os2;
   int32_t B, S, H, T;
   int32_t n_qt;             // query tiles per (batch, head)
-  int32_t grid;             // workgroups launched
-  // Tiles [0, n_whole) are computed by one workgroup each; the remaining
-  // n_split tiles by nsplit workgroups each over disjoint key ranges, whose
-  // partial (O, max, sum) go to `part` and are merged by a second launch.
-  int32_t n_whole;
-  int32_t n_split;
-  int32_t nsplit;
-  float* part;
+  int32_t grid;             // workgroups launched (single-problem kernels)
   float eps;
   float c2;                 // softmax scale * log2(e)
   float scale;
   Rope rope;
 };
+
+// Up to G problems in one attention launch (G = 1 for a plain call). Their
+// query tiles are numbered one after another: problem i owns global tiles
+// [tile_end[i-1], tile_end[i]). Global tiles [0, n_whole) are computed by one
+// workgroup each; the remaining n_split tiles by nsplit workgroups each over
+// disjoint key ranges, whose partial (O, max, sum) records go to `part` and
+// are merged by a second launch.
+template <int G>
+struct Group {
+  Args p[G];
+  int32_t tile_end[G];
+  int32_t n_whole;
+  int32_t n_split;
+  int32_t nsplit;
+  float* part;
+};
+
+// Problem owning global tile gt, and the tile's index within that problem.
+template <int G>
+__device__ __forceinline__ int group_problem(const Group<G>& g, int gt, int& tile) {
+  int k = 0;
+#pragma unroll
+  for (int i = 0; i + 1 < G; ++i) k += gt >= g.tile_end[i];
+  tile = k ? gt - g.tile_end[k - 1] : gt;
+  return k;
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -76,35 +76,22 @@ int check_strides(const int64_t* st, int dtype) {
   return MRA_OK;
 }
 
-// How the bf16 attention grid is laid out. When the last round of whole
-// query tiles would leave most resident slots idle, the last n_split tiles are
-// cut into nsplit key ranges each, computed by separate workgroups and merged.
+// How the bf16 attention grid of a group of problems is laid out (a plain
+// call is a group of one). Query tiles are numbered problem after problem.
+// When the last round of whole tiles would leave most resident slots idle, the
+// last n_split tiles are cut into nsplit key ranges each, computed by separate
+// workgroups and merged by a second kernel. The workspace holds, problem after
+// problem, the (cos, sin) table [B, S, D/2] float2 and (prepass K prologue
+// only) K' [B, H, S, D] bf16, then the fp32 split-tile records; every piece
+// starts 256-byte aligned.
 struct Plan {
-  int n_qt, tiles, n_whole, n_split, nsplit;
-  size_t part_floats;  // per split workgroup
+  int n;
+  int n_qt[MRA_MAX_GROUP];
+  int tile_end[MRA_MAX_GROUP];
+  int n_whole, n_split, nsplit;
+  size_t off_table[MRA_MAX_GROUP], off_kp[MRA_MAX_GROUP], off_part, bytes;
 };
 
-Plan make_plan(const mra_desc* d) {
-  Plan p;
-  p.n_qt = (d->seq + kBlockM - 1) / kBlockM;
-  p.tiles = d->batch * d->heads * p.n_qt;
-  const int ktiles = (d->seq + kBlockN - 1) / kBlockN;
-  int r = p.tiles >= kResidentSlots ? p.tiles % kResidentSlots : p.tiles;
-  int k = 1;
-  // split only when the last wave would leave at least half of the compute
-  // units idle (a unit running one workgroup instead of two is not idle)
-  if (r > 0 && 4 * r <= kResidentSlots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
-  if (k < 2) { r = 0; k = 1; }
-  p.n_split = r;
-  p.nsplit = k;
-  p.n_whole = p.tiles - r;
-  p.part_floats = (size_t)kRowBlocks * kWaves * 64 * (d->head_dim / 32 * 16 + 2);
-  return p;
-}
-
-// Workspace layout (bf16 path), each piece 256-byte aligned: the (cos, sin)
-// table [B, S, D/2] float2; K' [B, H, S, D] bf16 (prepass K prologue only);
-// split-tile partial records (fp32).
 size_t table_bytes(const mra_desc* d) {
   return round_up((size_t)d->batch * d->seq * (d->head_dim / 2) * sizeof(float2), kWsAlign);
 }
@@ -112,14 +99,43 @@ size_t kprime_bytes(const mra_desc* d) {
   if (resolve_kprologue(d) != MRA_KPRO_PREPASS) return 0;
   return round_up((size_t)d->batch * d->seq * d->heads * d->head_dim * sizeof(uint16_t), kWsAlign);
 }
-size_t part_bytes(const mra_desc* d) {
-  const Plan p = make_plan(d);
-  return round_up((size_t)p.n_split * p.nsplit * p.part_floats * sizeof(float), kWsAlign);
+
+// bf16 problems with at least one token; ds[i] valid (checked by the caller)
+Plan make_plan(const mra_desc* const* ds, int n) {
+  Plan p;
+  std::memset(&p, 0, sizeof(p));
+  p.n = n;
+  int tiles = 0, ktiles = 1 << 30;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    const mra_desc* d = ds[i];
+    p.n_qt[i] = (d->seq + kBlockM - 1) / kBlockM;
+    tiles += d->batch * d->heads * p.n_qt[i];
+    p.tile_end[i] = tiles;
+    ktiles = std::min(ktiles, (d->seq + kBlockN - 1) / kBlockN);
+    p.off_table[i] = off;
+    off += table_bytes(d);
+    p.off_kp[i] = off;
+    off += kprime_bytes(d);
+  }
+  int r = tiles >= kResidentSlots ? tiles % kResidentSlots : tiles;
+  int k = 1;
+  // split only when the last wave would leave at least half of the compute
+  // units idle (a unit running one workgroup instead of two is not idle)
+  if (r > 0 && 4 * r <= kResidentSlots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
+  if (k < 2) { r = 0; k = 1; }
+  p.n_split = r;
+  p.nsplit = k;
+  p.n_whole = tiles - r;
+  p.off_part = off;
+  const size_t rec_floats = (size_t)kRowBlocks * kWaves * 64 * (ds[0]->head_dim / 2 + 2);
+  p.bytes = off + round_up((size_t)r * k * rec_floats * sizeof(float), kWsAlign);
+  return p;
 }
 
 size_t workspace_bytes(const mra_desc* d) {
   if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0) return 0;
-  return table_bytes(d) + kprime_bytes(d) + part_bytes(d);
+  return make_plan(&d, 1).bytes;
 }
 
 void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const void* v,
@@ -143,6 +159,14 @@ void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const v
   a.rope.sec_th = d->section[0] + d->section[1];
 }
 
+// Points problem j's Args at its pieces of the workspace.
+void bind_workspace(Args& a, const mra_desc* d, const Plan& p, int j, void* workspace) {
+  char* w = (char*)workspace;
+  a.cs = (float2*)(w + p.off_table[j]);
+  a.kp = resolve_kprologue(d) == MRA_KPRO_PREPASS ? (uint16_t*)(w + p.off_kp[j]) : nullptr;
+  a.n_qt = p.n_qt[j];
+}
+
 template <int D>
 hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
   const int64_t tokens = (int64_t)a.B * a.S;
@@ -155,17 +179,46 @@ hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_attend_bf16(Args& a, int kpro, hipStream_t s) {
+template <int D, int G>
+hipError_t launch_attend_group(const mra::Group<G>& g, int kpro, hipStream_t s) {
+  const unsigned grid = (unsigned)(g.n_whole + g.n_split * g.nsplit);
   if (kpro == MRA_KPRO_PREPASS)
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, false>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, false, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
   else
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, true>), dim3(a.grid), dim3(kWaves * 64), 0, s, a);
-  if (a.n_split) {
-    const int64_t threads = (int64_t)a.n_split * kWaves * kRowBlocks * (D / 8) * 64;
-    hipLaunchKernelGGL((mra::split_merge_kernel<D, kWaves, kRowBlocks>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, true, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+  if (g.n_split) {
+    const int64_t threads = (int64_t)g.n_split * kWaves * kRowBlocks * (D / 8) * 64;
+    hipLaunchKernelGGL((mra::split_merge_kernel<D, kWaves, kRowBlocks, G>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, g);
   }
   return hipGetLastError();
+}
+static_assert(sizeof(mra::Group<MRA_MAX_GROUP>) <= 4096, "kernel argument size");
+
+// Group descriptor for the attention launch of the problems in `as`, which
+// fill_args and bind_workspace have prepared.
+template <int G>
+void make_group(mra::Group<G>& g, const Args* as, const Plan& p, void* workspace) {
+  std::memset(&g, 0, sizeof(g));
+  for (int i = 0; i < p.n; ++i) {
+    g.p[i] = as[i];
+    g.tile_end[i] = p.tile_end[i];
+  }
+  for (int i = p.n; i < G; ++i) g.tile_end[i] = p.tile_end[p.n - 1];
+  g.n_whole = p.n_whole;
+  g.n_split = p.n_split;
+  g.nsplit = p.nsplit;
+  g.part = p.n_split ? (float*)((char*)workspace + p.off_part) : nullptr;
+}
+
+hipError_t launch_attend(const Args* as, const Plan& p, void* workspace, int D, int kpro, hipStream_t s) {
+  if (p.n == 1) {
+    mra::Group<1> g;
+    make_group(g, as, p, workspace);
+    return D == 128 ? launch_attend_group<128>(g, kpro, s) : launch_attend_group<64>(g, kpro, s);
+  }
+  mra::Group<MRA_MAX_GROUP> g;
+  make_group(g, as, p, workspace);
+  return D == 128 ? launch_attend_group<128>(g, kpro, s) : launch_attend_group<64>(g, kpro, s);
 }
 
 template <int D>
@@ -180,7 +233,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 100; }
+int mrope_attn_abi_version(void) { return 101; }
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {
@@ -235,7 +288,7 @@ size_t mrope_attn_workspace_size(const mra_desc* d) {
 static int prepare_call(const mra_desc* d, const void* q, const void* k, const void* v,
                         const int32_t* pos, const float* gq, const float* gk,
                         const int32_t* seq_lens, void* out, float* lse, void* workspace,
-                        size_t ws_bytes, Args& a, bool& empty) {
+                        size_t ws_bytes, Args& a, Plan& plan, bool& empty) {
   int rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
   if (rc != MRA_OK) return rc;
   empty = d->batch == 0 || d->seq == 0;
@@ -247,18 +300,8 @@ static int prepare_call(const mra_desc* d, const void* q, const void* k, const v
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
   fill_args(a, d, q, k, v, pos, gq, gk, seq_lens, out, lse);
   if (d->dtype == MRA_BF16) {
-    char* w = (char*)workspace;
-    a.cs = (float2*)w;
-    w += table_bytes(d);
-    if (resolve_kprologue(d) == MRA_KPRO_PREPASS) a.kp = (uint16_t*)w;
-    w += kprime_bytes(d);
-    const Plan p = make_plan(d);
-    a.n_qt = p.n_qt;
-    a.n_whole = p.n_whole;
-    a.n_split = p.n_split;
-    a.nsplit = p.nsplit;
-    a.grid = p.n_whole + p.n_split * p.nsplit;
-    a.part = p.n_split ? (float*)w : nullptr;
+    plan = make_plan(&d, 1);
+    bind_workspace(a, d, plan, 0, workspace);
   }
   return MRA_OK;
 }
@@ -267,8 +310,9 @@ int mrope_attn_prepare(const mra_desc* d, const void* k, const int32_t* pos, con
                        void* workspace, size_t ws_bytes, void* stream) {
   // q/v/out/gamma_q are not touched by this stage; validate with k standing in
   Args a;
+  Plan plan;
   bool empty = false;
-  int rc = prepare_call(d, k, k, k, pos, gk, gk, nullptr, (void*)k, nullptr, workspace, ws_bytes, a, empty);
+  int rc = prepare_call(d, k, k, k, pos, gk, gk, nullptr, (void*)k, nullptr, workspace, ws_bytes, a, plan, empty);
   if (rc != MRA_OK || empty || d->dtype != MRA_BF16) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int kpro = resolve_kprologue(d);
@@ -280,17 +324,16 @@ int mrope_attn_attend(const mra_desc* d, const void* q, const void* k, const voi
                       const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
                       void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   Args a;
+  Plan plan;
   bool empty = false;
-  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, empty);
+  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, plan, empty);
   if (rc != MRA_OK || empty) return rc;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (d->dtype == MRA_FP32) {
+  if (d->dtype == MRA_FP32)
     e = d->head_dim == 128 ? launch_fp32<128>(a, s) : launch_fp32<64>(a, s);
-  } else {
-    const int kpro = resolve_kprologue(d);
-    e = d->head_dim == 128 ? launch_attend_bf16<128>(a, kpro, s) : launch_attend_bf16<64>(a, kpro, s);
-  }
+  else
+    e = launch_attend(&a, plan, workspace, d->head_dim, resolve_kprologue(d), s);
   return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
@@ -298,8 +341,9 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
                    const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
                    void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   Args a;
+  Plan plan;
   bool empty = false;
-  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, empty);
+  int rc = prepare_call(d, q, k, v, pos, gq, gk, seq_lens, out, lse, workspace, ws_bytes, a, plan, empty);
   if (rc != MRA_OK || empty) return rc;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -308,9 +352,75 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
   } else {
     const int kpro = resolve_kprologue(d);
     e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
-    if (e == hipSuccess)
-      e = d->head_dim == 128 ? launch_attend_bf16<128>(a, kpro, s) : launch_attend_bf16<64>(a, kpro, s);
+    if (e == hipSuccess) e = launch_attend(&a, plan, workspace, d->head_dim, kpro, s);
   }
+  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+// Problems of a group call that hold at least one token, in call order;
+// checks the group-wide conditions. Returns MRA_OK and their count in *m.
+static int group_members(const mra_desc* descs, const mra_problem* probs, int n, int* idx, int* m) {
+  if (!descs || !probs) return MRA_ERR_NULL;
+  if (n < 1 || n > MRA_MAX_GROUP) return MRA_ERR_PARAM;
+  *m = 0;
+  for (int i = 0; i < n; ++i) {
+    const mra_desc* d = &descs[i];
+    const mra_problem& p = probs[i];
+    int rc = mrope_attn_validate(d, p.q, p.k, p.v, p.pos_thw, p.gamma_q, p.gamma_k, p.seq_lens, p.out);
+    if (rc != MRA_OK) return rc;
+    if (p.lse && !aligned(p.lse, 4)) return MRA_ERR_STRIDE;
+    if (d->dtype != descs[0].dtype || d->head_dim != descs[0].head_dim) return MRA_ERR_UNSUPPORTED;
+    if (d->dtype == MRA_BF16 && resolve_kprologue(d) != resolve_kprologue(&descs[0])) return MRA_ERR_UNSUPPORTED;
+    if (d->batch > 0 && d->seq > 0) idx[(*m)++] = i;
+  }
+  return MRA_OK;
+}
+
+size_t mrope_attn_group_workspace_size(const mra_desc* descs, int n) {
+  if (!descs || n < 1 || n > MRA_MAX_GROUP) return 0;
+  const mra_desc* ds[MRA_MAX_GROUP];
+  int m = 0;
+  for (int i = 0; i < n; ++i) {
+    if (check_desc(&descs[i]) != MRA_OK) return 0;
+    if (descs[i].dtype != descs[0].dtype || descs[i].head_dim != descs[0].head_dim) return 0;
+    if (descs[i].batch > 0 && descs[i].seq > 0) ds[m++] = &descs[i];
+  }
+  if (m == 0 || descs[0].dtype != MRA_BF16) return 0;
+  return make_plan(ds, m).bytes;
+}
+
+int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  int idx[MRA_MAX_GROUP], m = 0;
+  int rc = group_members(descs, probs, n, idx, &m);
+  if (rc != MRA_OK) return rc;
+  if (m == 0) return MRA_OK;
+  const size_t need = mrope_attn_group_workspace_size(descs, n);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  Args as[MRA_MAX_GROUP];
+  const mra_desc* ds[MRA_MAX_GROUP];
+  for (int j = 0; j < m; ++j) {
+    const mra_problem& p = probs[idx[j]];
+    ds[j] = &descs[idx[j]];
+    fill_args(as[j], ds[j], p.q, p.k, p.v, p.pos_thw, p.gamma_q, p.gamma_k, p.seq_lens, p.out, p.lse);
+  }
+  const int D = descs[0].head_dim;
+  hipError_t e = hipSuccess;
+  if (descs[0].dtype == MRA_FP32) {
+    for (int j = 0; j < m && e == hipSuccess; ++j)
+      e = D == 128 ? launch_fp32<128>(as[j], s) : launch_fp32<64>(as[j], s);
+    return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  }
+  const Plan plan = make_plan(ds, m);
+  const int kpro = resolve_kprologue(ds[0]);
+  for (int j = 0; j < m && e == hipSuccess; ++j) {
+    bind_workspace(as[j], ds[j], plan, j, workspace);
+    e = D == 128 ? launch_prologue_bf16<128>(as[j], kpro, s) : launch_prologue_bf16<64>(as[j], kpro, s);
+  }
+  if (e == hipSuccess) e = launch_attend(as, plan, workspace, D, kpro, s);
   return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

@@ -38,8 +38,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_fwd", "mrope_attn_prepare",
-        "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_workspace_size"])
+        "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_fwd", "mrope_attn_fwd_group",
+        "mrope_attn_group_workspace_size", "mrope_attn_prepare", "mrope_attn_status_string",
+        "mrope_attn_validate", "mrope_attn_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -50,6 +51,11 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
+def test_problem_layout_matches_header(lib):
+    assert ctypes.sizeof(B.Problem) == 9 * 8
+    assert B.Problem.out.offset == 56
+
+
 def test_desc_layout_matches_header(lib):
     # 11 int32/float fields + 3 + 12 int64 strides; int64 block aligned at 8
     assert ctypes.sizeof(B.Desc) == 4 * 13 + 4 + 8 * 12
@@ -57,7 +63,7 @@ def test_desc_layout_matches_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 100
+    assert lib.mrope_attn_abi_version() == 101
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -192,3 +198,54 @@ def test_binding_refuses_cpu_tensors(lib):
     with pytest.raises(ValueError):
         B.mrope_attn(x, x, x, torch.zeros(1, 4, 3, dtype=torch.int32), torch.ones(64),
                      torch.ones(64), text_pad=0, section=(8, 12, 12))
+
+
+# ---------------------------------------------------------------- grouped call
+def _group(descs, probs=None, ws=FAKE, nbytes=1 << 40):
+    n = len(descs)
+    darr = (B.Desc * max(n, 1))(*descs)
+    if probs is None:
+        probs = [B.Problem(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) for _ in descs]
+    parr = (B.Problem * max(n, 1))(*probs)
+    return B.lib().mrope_attn_fwd_group(darr, parr, n, ws, nbytes, None)
+
+
+def test_group_workspace_is_the_sum_of_its_parts(lib):
+    cond = desc(batch=1, seq=4608, heads=32, text_pad=512)
+    uncond = desc(batch=1, seq=4096, heads=32, text_pad=0)
+    # per problem: rotary table + K'; then the split records of the combined
+    # grid: 1152 + 1024 = 2176 tiles leave 128 for the last wave -> 2 parts
+    per = [s * 64 * 8 + s * 32 * 128 * 2 for s in (4608, 4096)]
+    split = 128 * 2 * 256 * (128 // 2 + 2) * 4
+    assert B.group_workspace_size([cond, uncond]) == sum(per) + split
+    # a group of one is the plain call
+    assert B.group_workspace_size([cond]) == B.workspace_size(cond)
+    # empty members take nothing; fp32 groups need none
+    assert B.group_workspace_size([cond, desc(batch=0)]) == B.workspace_size(cond)
+    f32 = dict(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))
+    assert B.group_workspace_size([desc(**f32), desc(**f32)]) == 0
+    # invalid or mixed groups -> 0
+    assert B.group_workspace_size([cond, desc(head_dim=64, section=(8, 12, 12))]) == 0
+    assert B.group_workspace_size([cond, desc(section=(1, 2, 3))]) == 0
+
+
+def test_group_rejects_before_launch(lib, monkeypatch):
+    d = desc()
+    assert _group([]) == -9                                     # n = 0
+    assert _group([d] * 5) == -9                                # n > MRA_MAX_GROUP
+    L = B.lib()
+    assert L.mrope_attn_fwd_group(None, None, 1, FAKE, 1 << 40, None) == -1
+    assert _group([d, desc(head_dim=64, section=(8, 12, 12))]) == -6
+    assert _group([d, desc(kprologue="fused")]) == -6
+    assert _group([d, desc(section=(1, 2, 3))]) == -4          # per-problem validation
+    bad = B.Problem(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None)
+    good = B.Problem(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None)
+    assert _group([d, d], [good, bad]) == -1
+    assert _group([d, d], [good, B.Problem(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2)]) == -5
+    need = B.group_workspace_size([d, d])
+    assert _group([d, d], ws=FAKE, nbytes=need - 1) == -7
+    assert _group([d, d], ws=None, nbytes=need) == -7
+    assert _group([desc(batch=0), desc(seq=0, text_pad=0)], ws=None, nbytes=0) == 0   # nothing to do
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _group([d, d], nbytes=need) == -8
+    assert _group([d, desc(batch=3, seq=40, text_pad=0)], nbytes=need) == -8
