@@ -79,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_fwd_group.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Problem), ctypes.c_int,
                                            vp, ctypes.c_size_t, vp]
         L.mrope_attn_fwd_group.restype = ctypes.c_int
+        L.mrope_attn_varlen_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
+        L.mrope_attn_varlen_workspace_size.restype = ctypes.c_size_t
+        L.mrope_attn_fwd_varlen.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p,
+                                            ctypes.c_int32, vp, f32p, vp, ctypes.c_size_t, vp]
+        L.mrope_attn_fwd_varlen.restype = ctypes.c_int
         L.mrope_attn_abi_version.argtypes = []
         L.mrope_attn_abi_version.restype = ctypes.c_int
         _lib = L
@@ -263,3 +268,43 @@ def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", wo
     if rc != 0:
         raise MraError(rc, status_string(rc))
     return results
+
+
+def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: int, *,
+                      section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
+                      scale=None, return_lse: bool = False, kprologue="auto", out=None,
+                      workspace=None):
+    """Packed variable-length form: q, k, v [T, H, D], pos [T, 3] int32,
+    cu_seqlens [B + 1] int32 on the GPU (sequence b = tokens cu[b]:cu[b+1]),
+    max_seqlen >= every sequence length. Returns out [T, H, D] (and lse
+    [H, T] if asked)."""
+    import torch
+
+    if q.dim() != 3:
+        raise ValueError("q, k, v must be [T, H, D] for the packed form")
+    t, h, d = q.shape
+    if pos.dim() != 2:
+        raise ValueError("pos must be [T, 3] for the packed form")
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a GPU int32 [B + 1] tensor")
+    cu_seqlens = cu_seqlens.contiguous()
+    nseq = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty((t, h, d), dtype=q.dtype, device=q.device)
+    desc, out4, lse, _ = _checked(q[None], k[None], v[None], pos[None], gamma_q, gamma_k, None,
+                                  out[None], False, text_pad=0, section=section, theta=theta,
+                                  eps=eps, scale=scale, kprologue=kprologue)
+    lse = torch.empty((h, t), dtype=torch.float32, device=q.device) if return_lse else None
+    desc.batch = nseq
+    need = int(lib().mrope_attn_varlen_workspace_size(ctypes.byref(desc), int(max_seqlen)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mrope_attn_fwd_varlen(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     pos.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                                     cu_seqlens.data_ptr(), int(max_seqlen), out.data_ptr(),
+                                     None if lse is None else lse.data_ptr(),
+                                     None if not need else workspace.data_ptr(), need, stream)
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return (out, lse) if return_lse else out

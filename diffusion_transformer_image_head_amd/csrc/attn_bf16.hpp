@@ -146,9 +146,12 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   const Args& a = gp.p[group_problem(gp, gt, tile)];
   const int qt = tile % a.n_qt, bh = tile / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
-  const int S = a.S, T = a.T;
+  const SeqView sv = seq_view(a, b);
+  const int S = sv.S, T = a.T, Sx = a.S, bl = sv.bl;
+  const int64_t tok0 = sv.tok0;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
   const int q0 = qt * BM;
+  if (q0 >= S) return;  // packed layout: tile past this item's end
   int row[RB];
   bool in_seq[RB], valid_row[RB];
   uint16_t* outp[RB];
@@ -158,8 +161,8 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     row[rb] = q0 + (wave * RB + rb) * 32 + m;
     in_seq[rb] = row[rb] < S;
     valid_row[rb] = in_seq[rb] && !(row[rb] >= L && row[rb] < T);
-    outp[rb] = (uint16_t*)a.out + b * a.os0 + (int64_t)row[rb] * a.os1 + head * a.os2;
-    lsep[rb] = a.lse ? a.lse + ((int64_t)b * a.H + head) * S + row[rb] : nullptr;
+    outp[rb] = (uint16_t*)a.out + bl * a.os0 + (tok0 + row[rb]) * a.os1 + head * a.os2;
+    lsep[rb] = a.lse ? a.lse + ((int64_t)bl * a.H + head) * Sx + tok0 + row[rb] : nullptr;
   }
 
   // Query tile made only of padded text slots: zeros, no attention.
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   for (int rb = 0; rb < RB; ++rb) {
     float x[KC][8];
     if (in_seq[rb]) {
-      const uint16_t* src = (const uint16_t*)a.q + b * a.qs0 + (int64_t)row[rb] * a.qs1 + head * a.qs2;
+      const uint16_t* src = (const uint16_t*)a.q + bl * a.qs0 + (tok0 + row[rb]) * a.qs1 + head * a.qs2;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const u32x4 w = *(const u32x4*)(src + c * 16 + hf * 8);
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     const float r = rsqrtf(ss * (1.0f / D) + a.eps);
     const float c2 = a.c2;
     // (cos, sin) of this token's pairs from the table the prologue pass wrote
-    const float2* csrow = a.cs + ((int64_t)b * S + min(row[rb], S - 1)) * (D / 2);
+    const float2* csrow = a.cs + ((int64_t)bl * Sx + tok0 + min(row[rb], S - 1)) * (D / 2);
 #pragma unroll
     for (int c = 0; c < KC / 2; ++c) {
       const f32x4 g1a = *(const f32x4*)(a.gq + c * 16 + hf * 8);
@@ -252,11 +255,11 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   // ---- operand sources. All bounds live in the per-lane offset: a row that
   // must not be read gets an offset at the resource size, which reads zeros.
   const int64_t krow = KFUSED ? a.ks1 : D;  // elements between K rows
-  const uint16_t* kbase = KFUSED ? (const uint16_t*)a.k + b * a.ks0 + head * a.ks2
-                                 : a.kp + ((int64_t)b * a.H + head) * S * D;
+  const uint16_t* kbase = KFUSED ? (const uint16_t*)a.k + bl * a.ks0 + tok0 * a.ks1 + head * a.ks2
+                                 : a.kp + (((int64_t)bl * a.H + head) * Sx + tok0) * D;
   const uint32_t knrec = (uint32_t)(((int64_t)(S - 1) * krow + D) * 2);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, knrec);
-  const uint16_t* vbase = (const uint16_t*)a.v + b * a.vs0 + head * a.vs2;
+  const uint16_t* vbase = (const uint16_t*)a.v + bl * a.vs0 + tok0 * a.vs1 + head * a.vs2;
   const uint32_t vnrec = (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, vnrec);
 
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
         const uint32_t off = key_ok(n) ? (uint32_t)((n * krow + fk_c[i] * 8) * 2) : knrec;
         fkr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
         const int j0 = (fk_c[i] % (CPR / 2)) * 8 + (fk_c[i] >= CPR / 2 ? 4 : 0);
-        const float2* cp = a.cs + ((int64_t)b * S + min(n, S - 1)) * (D / 2) + j0;
+        const float2* cp = a.cs + ((int64_t)bl * Sx + tok0 + min(n, S - 1)) * (D / 2) + j0;
         // lanes c and c^1 share one group of 8 pair angles: each fetches 4
 #pragma unroll
         for (int e = 0; e < 4; ++e) fcs[i][e] = cp[e];
@@ -632,7 +635,9 @@ __global__ __launch_bounds__(256) void split_merge_kernel(Group<G> gp) {
   const Args& a = gp.p[group_problem(gp, gp.n_whole + st, tile)];
   const int qt = tile % a.n_qt, bh = tile / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
-  const int S = a.S, T = a.T;
+  const SeqView sv = seq_view(a, b);
+  const int S = sv.S, T = a.T, bl = sv.bl;
+  const int64_t tok0 = sv.tok0;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
   const int q0 = qt * BM;
   // a tile made only of padded text slots was written by the attention kernel
@@ -675,10 +680,10 @@ __global__ __launch_bounds__(256) void split_merge_kernel(Group<G> gp) {
   w0 = valid_row ? w0 : 0u;
   w1 = valid_row ? w1 : 0u;
   const int db = c >> 2, g = c & 3;
-  uint16_t* outp = (uint16_t*)a.out + b * a.os0 + (int64_t)row * a.os1 + head * a.os2;
+  uint16_t* outp = (uint16_t*)a.out + bl * a.os0 + (tok0 + row) * a.os1 + head * a.os2;
   *(u32x2*)(outp + db * 32 + g * 8 + hf * 4) = u32x2{w0, w1};
   if (a.lse && c == 0 && hf == 0)
-    a.lse[((int64_t)b * a.H + head) * S + row] = valid_row ? m_all * kLn2 + logf(l_all) : -INFINITY;
+    a.lse[((int64_t)bl * a.H + head) * a.S + tok0 + row] = valid_row ? m_all * kLn2 + logf(l_all) : -INFINITY;
 }
 
 }  // namespace mra

@@ -43,8 +43,11 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
   const int bid = blockIdx.x;
   const int qt = bid % a.n_qt, bh = bid / a.n_qt;
   const int head = bh % a.H, b = bh / a.H;
-  const int S = a.S, T = a.T;
+  const SeqView sv = seq_view(a, b);
+  const int S = sv.S, T = a.T, Sx = a.S, bl = sv.bl;
+  const int64_t tok0 = sv.tok0;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
+  if (qt * BM >= S) return;  // packed layout: tile past this item's end
   const int row = qt * BM + t;
   const bool in_seq = row < S;
   const bool valid_row = in_seq && !(row >= L && row < T);
@@ -53,9 +56,9 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
   const float* v = (const float*)a.v;
 
   if (in_seq) {
-    const float* src = q + b * a.qs0 + row * a.qs1 + head * a.qs2;
+    const float* src = q + bl * a.qs0 + (tok0 + row) * a.qs1 + head * a.qs2;
     for (int d = 0; d < D; ++d) Qs[t][d] = src[d];
-    const int32_t* p3 = a.pos + ((int64_t)b * S + row) * 3;
+    const int32_t* p3 = a.pos + ((int64_t)bl * Sx + tok0 + row) * 3;
     prologue_row_f32<D>(Qs[t], a.gq, a.rope, p3[0], p3[1], p3[2], a.eps);
   }
 
@@ -68,16 +71,16 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
     if (t < BN) {
       const int n = n0 + t;
       if (n < S) {
-        const float* src = k + b * a.ks0 + n * a.ks1 + head * a.ks2;
+        const float* src = k + bl * a.ks0 + (tok0 + n) * a.ks1 + head * a.ks2;
         for (int d = 0; d < D; ++d) Ks[t][d] = src[d];
-        const int32_t* p3 = a.pos + ((int64_t)b * S + n) * 3;
+        const int32_t* p3 = a.pos + ((int64_t)bl * Sx + tok0 + n) * 3;
         prologue_row_f32<D>(Ks[t], a.gk, a.rope, p3[0], p3[1], p3[2], a.eps);
       }
     }
     for (int i = t; i < BN * D; i += 64) {
       const int kk = i / D, d = i - kk * D;
       const int n = n0 + kk;
-      Vs[kk][d] = n < S ? v[b * a.vs0 + n * a.vs1 + head * a.vs2 + d] : 0.f;
+      Vs[kk][d] = n < S ? v[bl * a.vs0 + (tok0 + n) * a.vs1 + head * a.vs2 + d] : 0.f;
     }
     __syncthreads();
     if (!valid_row) continue;
@@ -99,10 +102,10 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
     }
   }
   if (!in_seq) return;
-  float* dst = (float*)a.out + b * a.os0 + row * a.os1 + head * a.os2;
+  float* dst = (float*)a.out + bl * a.os0 + (tok0 + row) * a.os1 + head * a.os2;
   const float inv = valid_row ? 1.0f / lrun : 0.f;
   for (int d = 0; d < D; ++d) dst[d] = valid_row ? o[d] * inv : 0.f;
-  if (a.lse) a.lse[((int64_t)b * a.H + head) * S + row] = valid_row ? mrun + logf(lrun) : -INFINITY;
+  if (a.lse) a.lse[((int64_t)bl * a.H + head) * Sx + tok0 + row] = valid_row ? mrun + logf(lrun) : -INFINITY;
 }
 
 }  // namespace mra

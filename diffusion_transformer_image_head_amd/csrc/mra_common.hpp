@@ -36,6 +36,7 @@ struct Args {
   const float* gq;          // [D]
   const float* gk;          // [D]
   const int32_t* seq_lens;  // [B] or null
+  const int32_t* cu_seqlens;  // [B + 1] or null: packed sequences (see seq_view)
   void* out;
   float* lse;               // [B, H, S] or null
   uint16_t* kp;             // K' (bf16) [B, H, S, D] in the workspace, or null
@@ -52,6 +53,22 @@ struct Args {
   float scale;
   Rope rope;
 };
+
+// Where batch item b's tokens sit in the tensors. Padded layout (no
+// cu_seqlens): item b holds tokens [0, S) of its own [S, ...] slice. Packed
+// layout: one [S_total, ...] slice (a.S = S_total) holds item b's tokens at
+// [cu_seqlens[b], cu_seqlens[b+1]), clamped into [0, S_total].
+struct SeqView {
+  int bl;        // batch index into the tensors
+  int64_t tok0;  // first token of the item within that slice
+  int S;         // tokens of the item
+};
+__device__ __forceinline__ SeqView seq_view(const Args& a, int b) {
+  if (!a.cu_seqlens) return SeqView{b, 0, a.S};
+  const int t0 = min(max(a.cu_seqlens[b], 0), a.S);
+  const int t1 = min(max(a.cu_seqlens[b + 1], t0), a.S);
+  return SeqView{0, t0, t1 - t0};
+}
 
 // Up to G problems in one attention launch (G = 1 for a plain call). Their
 // query tiles are numbered one after another: problem i owns global tiles

@@ -100,8 +100,12 @@ size_t kprime_bytes(const mra_desc* d) {
   return round_up((size_t)d->batch * d->seq * d->heads * d->head_dim * sizeof(uint16_t), kWsAlign);
 }
 
-// bf16 problems with at least one token; ds[i] valid (checked by the caller)
-Plan make_plan(const mra_desc* const* ds, int n) {
+// bf16 problems with at least one token; ds[i] valid (checked by the caller).
+// Problem i's query tiles cover qbatch[i] items of qlen[i] rows (defaults:
+// the descriptor's batch and seq; a packed layout passes its item count and
+// longest item), its table and K' the descriptor's [batch, seq] layout.
+Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
+               const int* qlen = nullptr) {
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.n = n;
@@ -109,10 +113,11 @@ Plan make_plan(const mra_desc* const* ds, int n) {
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
     const mra_desc* d = ds[i];
-    p.n_qt[i] = (d->seq + kBlockM - 1) / kBlockM;
-    tiles += d->batch * d->heads * p.n_qt[i];
+    const int qb = qbatch ? qbatch[i] : d->batch, ql = qlen ? qlen[i] : d->seq;
+    p.n_qt[i] = (ql + kBlockM - 1) / kBlockM;
+    tiles += qb * d->heads * p.n_qt[i];
     p.tile_end[i] = tiles;
-    ktiles = std::min(ktiles, (d->seq + kBlockN - 1) / kBlockN);
+    ktiles = std::min(ktiles, (ql + kBlockN - 1) / kBlockN);
     p.off_table[i] = off;
     off += table_bytes(d);
     p.off_kp[i] = off;
@@ -221,9 +226,11 @@ hipError_t launch_attend(const Args* as, const Plan& p, void* workspace, int D, 
   return D == 128 ? launch_attend_group<128>(g, kpro, s) : launch_attend_group<64>(g, kpro, s);
 }
 
+// qlen: rows per item (a.S for the padded layout, the longest item for a
+// packed one)
 template <int D>
-hipError_t launch_fp32(Args& a, hipStream_t s) {
-  a.n_qt = (a.S + kFp32BlockM - 1) / kFp32BlockM;
+hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
+  a.n_qt = (qlen + kFp32BlockM - 1) / kFp32BlockM;
   a.grid = a.B * a.H * a.n_qt;
   hipLaunchKernelGGL(mra::attn_fp32_kernel<D>, dim3(a.grid), dim3(64), 0, s, a);
   return hipGetLastError();
@@ -233,7 +240,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 101; }
+int mrope_attn_abi_version(void) { return 102; }
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {
@@ -331,7 +338,7 @@ int mrope_attn_attend(const mra_desc* d, const void* q, const void* k, const voi
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (d->dtype == MRA_FP32)
-    e = d->head_dim == 128 ? launch_fp32<128>(a, s) : launch_fp32<64>(a, s);
+    e = d->head_dim == 128 ? launch_fp32<128>(a, s, a.S) : launch_fp32<64>(a, s, a.S);
   else
     e = launch_attend(&a, plan, workspace, d->head_dim, resolve_kprologue(d), s);
   return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
@@ -348,7 +355,7 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (d->dtype == MRA_FP32) {
-    e = d->head_dim == 128 ? launch_fp32<128>(a, s) : launch_fp32<64>(a, s);
+    e = d->head_dim == 128 ? launch_fp32<128>(a, s, a.S) : launch_fp32<64>(a, s, a.S);
   } else {
     const int kpro = resolve_kprologue(d);
     e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
@@ -411,7 +418,7 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
   hipError_t e = hipSuccess;
   if (descs[0].dtype == MRA_FP32) {
     for (int j = 0; j < m && e == hipSuccess; ++j)
-      e = D == 128 ? launch_fp32<128>(as[j], s) : launch_fp32<64>(as[j], s);
+      e = D == 128 ? launch_fp32<128>(as[j], s, as[j].S) : launch_fp32<64>(as[j], s, as[j].S);
     return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
   }
   const Plan plan = make_plan(ds, m);
@@ -421,6 +428,70 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
     e = D == 128 ? launch_prologue_bf16<128>(as[j], kpro, s) : launch_prologue_bf16<64>(as[j], kpro, s);
   }
   if (e == hipSuccess) e = launch_attend(as, plan, workspace, D, kpro, s);
+  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+// ---- packed variable-length sequences (cu_seqlens) ------------------------
+// The descriptor describes the packed layout: seq = total tokens, batch =
+// number of sequences; tensors are one [seq, H, D] slice (the batch stride is
+// not used), pos_thw [seq, 3], lse [H, seq].
+static int varlen_layout(const mra_desc* d, int32_t max_seqlen, mra_desc& lay) {
+  int rc = check_desc(d);
+  if (rc != MRA_OK) return rc;
+  if (d->text_pad != 0) return MRA_ERR_SHAPE;
+  if (max_seqlen < 0 || max_seqlen > d->seq) return MRA_ERR_SHAPE;
+  lay = *d;
+  lay.batch = 1;
+  return MRA_OK;
+}
+
+size_t mrope_attn_varlen_workspace_size(const mra_desc* d, int32_t max_seqlen) {
+  mra_desc lay;
+  if (varlen_layout(d, max_seqlen, lay) != MRA_OK) return 0;
+  if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0 || max_seqlen == 0) return 0;
+  const mra_desc* ds[1] = {&lay};
+  const int qb = d->batch, ql = max_seqlen;
+  return make_plan(ds, 1, &qb, &ql).bytes;
+}
+
+int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const void* v,
+                          const int32_t* pos, const float* gq, const float* gk,
+                          const int32_t* cu_seqlens, int32_t max_seqlen, void* out, float* lse,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  mra_desc lay;
+  int rc = varlen_layout(d, max_seqlen, lay);
+  if (rc != MRA_OK) return rc;
+  if (d->batch == 0 || d->seq == 0 || max_seqlen == 0) return MRA_OK;
+  rc = mrope_attn_validate(&lay, q, k, v, pos, gq, gk, nullptr, out);
+  if (rc != MRA_OK) return rc;
+  if (!cu_seqlens) return MRA_ERR_NULL;
+  if (!aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4))) return MRA_ERR_STRIDE;
+  const size_t need = mrope_attn_varlen_workspace_size(d, max_seqlen);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  Args a;
+  fill_args(a, &lay, q, k, v, pos, gq, gk, nullptr, out, lse);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d->dtype == MRA_FP32) {
+    a.B = d->batch;
+    a.cu_seqlens = cu_seqlens;
+    e = d->head_dim == 128 ? launch_fp32<128>(a, s, max_seqlen) : launch_fp32<64>(a, s, max_seqlen);
+  } else {
+    const mra_desc* ds[1] = {&lay};
+    const int qb = d->batch, ql = max_seqlen;
+    const Plan plan = make_plan(ds, 1, &qb, &ql);
+    bind_workspace(a, &lay, plan, 0, workspace);
+    const int kpro = resolve_kprologue(d);
+    // the prologue pass runs over the packed layout (one item of seq tokens)
+    e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
+    if (e == hipSuccess) {
+      a.B = d->batch;
+      a.cu_seqlens = cu_seqlens;
+      e = launch_attend(&a, plan, workspace, d->head_dim, kpro, s);
+    }
+  }
   return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

@@ -132,3 +132,43 @@ def make_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w,
 def config_workload(name: str) -> Workload:
     """The named configuration with its own seed."""
     return make_workload(**CONFIGS[name])
+
+
+@dataclass
+class VarlenWorkload:
+    """Sequences packed back to back (no padding): q, k, v [T, H, D],
+    pos [T, 3], cu_seqlens [B + 1]."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    pos: np.ndarray
+    gamma_q: np.ndarray
+    gamma_k: np.ndarray
+    cu_seqlens: np.ndarray
+    section: tuple
+    dtype: str
+    theta: float = 10000.0
+    eps: float = 1e-6
+
+    @property
+    def max_seqlen(self):
+        return int(np.max(np.diff(self.cu_seqlens))) if len(self.cu_seqlens) > 1 else 0
+
+    def flops(self):
+        _, h, d = self.q.shape
+        return 4 * h * d * int(sum(int(n) ** 2 for n in np.diff(self.cu_seqlens)))
+
+
+def make_varlen_workload(heads, head_dim, section, text_lens, grids, sigma=1.0, dtype="bf16",
+                         seed=0) -> VarlenWorkload:
+    """Sequence b = text_lens[b] real text tokens then a grids[b] = (gh, gw)
+    image raster, each drawn as its own unpadded one-item workload (seed +
+    b), with the first item's gammas shared by all."""
+    parts = [make_workload(1, heads, head_dim, section, int(l), gh, gw, sigma=sigma, dtype=dtype,
+                           seed=seed + b) for b, (l, (gh, gw)) in enumerate(zip(text_lens, grids))]
+    lens = [p.q.shape[1] for p in parts]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cat = lambda f: np.ascontiguousarray(np.concatenate([getattr(p, f)[0] for p in parts]))  # noqa: E731
+    return VarlenWorkload(q=cat("q"), k=cat("k"), v=cat("v"), pos=cat("pos"),
+                          gamma_q=parts[0].gamma_q, gamma_k=parts[0].gamma_k, cu_seqlens=cu,
+                          section=tuple(section), dtype=dtype)

@@ -178,6 +178,28 @@ size_t mrope_attn_group_workspace_size(const mra_desc* descs, int n);
 int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Packed variable-length sequences -----------------------------------
+ *
+ * The per-prompt text length can also be carried by packing instead of
+ * padding (the padding convention is the SimpleTuner quickstart's "Text Embed
+ * Cache"; packing drops the padded slots): desc->batch sequences of varying
+ * length are stored back to back, sequence b holding tokens
+ * [cu_seqlens[b], cu_seqlens[b+1]) of one [desc->seq, H, D] slice (its own
+ * true-length text tokens followed by its image tokens, each with its (t, h, w)
+ * in pos_thw), and every token attends to the tokens of its own sequence
+ * only. desc->seq is the total token count, desc->text_pad must be 0
+ * (MRA_ERR_SHAPE), the batch strides are not used, pos_thw is [seq, 3] and
+ * lse [H, seq]. cu_seqlens is a device [batch + 1] int32 array, read on the
+ * device and clamped into [0, seq]; max_seqlen (0..seq, else MRA_ERR_SHAPE)
+ * must be at least every sequence's length: rows past max_seqlen of a longer
+ * sequence are not computed. Tokens outside every sequence are not written. */
+size_t mrope_attn_varlen_workspace_size(const mra_desc* desc, int32_t max_seqlen);
+
+int mrope_attn_fwd_varlen(const mra_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                          const int32_t* cu_seqlens, int32_t max_seqlen, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* mrope_attn_status_string(int status);
 

@@ -171,3 +171,32 @@ def oracle_fwd(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     kr = mrope(rms_norm(k, gamma_k, eps), pos, section, theta)
     valid = valid_tokens(b_, s_, text_pad, seq_lens)
     return attention(qr, kr, v, valid, scale, rows=rows, heads=heads)
+
+
+def oracle_fwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, *, section=(16, 24, 24),
+                      theta: float = 10000.0, eps: float = 1e-6, scale=None):
+    """Packed variable-length form of the same path: sequence b is tokens
+    [cu_seqlens[b], cu_seqlens[b+1]) of q, k, v [T, H, D] and pos [T, 3] (its
+    true-length text tokens, then its image tokens), and attends to its own
+    tokens only (the per-prompt true text length of the SimpleTuner
+    quickstart's "Text Embed Cache", carried by packing instead of padding).
+    Each sequence is the padding-free case of :func:`oracle_fwd`.
+
+    Returns (out [T, H, D], lse [H, T]) in float64; tokens outside every
+    sequence are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    t_, h_, d_ = q.shape
+    out = np.full((t_, h_, d_), np.nan)
+    lse = np.full((h_, t_), np.nan)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        a0, a1 = int(cu[b]), int(cu[b + 1])
+        if a1 <= a0:
+            continue
+        o, l = oracle_fwd(q[None, a0:a1], np.asarray(k)[None, a0:a1], np.asarray(v)[None, a0:a1],
+                          np.asarray(pos)[None, a0:a1], gamma_q, gamma_k, None, text_pad=0,
+                          section=section, theta=theta, eps=eps, scale=scale)
+        out[a0:a1] = o[0]
+        lse[:, a0:a1] = l[0]
+    return out, lse

@@ -366,4 +366,71 @@ def pin_page_geometry():
     assert [int((ax == a).sum()) for a in range(3)] == list(sec)
 
 
+# --------------------------------------------------------------------- packed varlen
+def _varlen_case():
+    from diffusion_transformer_image_head_amd.workloads import make_varlen_workload
+    return make_varlen_workload(2, 16, (2, 3, 3), text_lens=(3, 0, 5), grids=((2, 3), (3, 3), (1, 2)),
+                                dtype="fp32", seed=60)
+
+
+def pin_varlen_brute():
+    """Packed sequences: each sequence by the scalar loops, on its own."""
+    w = _varlen_case()
+    out, lse = ref.oracle_fwd_varlen(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens,
+                                     section=w.section)
+    cu = w.cu_seqlens
+    for b in range(len(cu) - 1):
+        a0, a1 = int(cu[b]), int(cu[b + 1])
+        bo, bl = brute_fwd(w.q[None, a0:a1].tolist(), w.k[None, a0:a1].tolist(),
+                           w.v[None, a0:a1].tolist(), w.pos[None, a0:a1].tolist(),
+                           w.gamma_q.tolist(), w.gamma_k.tolist(), None, text_pad=0,
+                           section=w.section, theta=w.theta, eps=w.eps)
+        assert np.max(np.abs(out[a0:a1] - np.array(bo)[0])) < 1e-12
+        assert np.max(np.abs(lse[:, a0:a1] - np.array(bl)[0])) < 1e-12
+
+
+def pin_varlen_equals_padded_batch():
+    """Packing and in-memory padding carry the same per-prompt text length:
+    the packed result equals the padded batch's on the real tokens."""
+    lens, gh, gw, pad = (3, 0, 6), 2, 3, 6
+    from diffusion_transformer_image_head_amd.workloads import make_varlen_workload
+    w = make_varlen_workload(2, 16, (2, 3, 3), text_lens=lens, grids=[(gh, gw)] * 3, dtype="fp32",
+                             seed=61)
+    out, lse = ref.oracle_fwd_varlen(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens,
+                                     section=w.section)
+    s = pad + gh * gw
+    shp = (3, s, 2, 16)
+    qp, kp, vp = np.zeros(shp), np.zeros(shp), np.zeros(shp)
+    pp = np.zeros((3, s, 3), dtype=np.int32)
+    for b, l in enumerate(lens):
+        a0 = int(w.cu_seqlens[b])
+        idx = list(range(l)) + list(range(pad, s))        # real slots in the padded item
+        for j, t in enumerate(idx):
+            qp[b, t], kp[b, t], vp[b, t], pp[b, t] = w.q[a0 + j], w.k[a0 + j], w.v[a0 + j], w.pos[a0 + j]
+    po, pl = ref.oracle_fwd(qp, kp, vp, pp, w.gamma_q, w.gamma_k, np.array(lens), text_pad=pad,
+                            section=w.section)
+    for b, l in enumerate(lens):
+        a0 = int(w.cu_seqlens[b])
+        idx = list(range(l)) + list(range(pad, s))
+        assert np.max(np.abs(po[b, idx] - out[a0:a0 + len(idx)])) < 1e-12
+        assert np.max(np.abs(pl[b][:, idx] - lse[:, a0:a0 + len(idx)])) < 1e-12
+
+
+def pin_varlen_sequences_are_isolated():
+    """Changing one sequence leaves every other sequence's output as it was."""
+    w = _varlen_case()
+    out, _ = ref.oracle_fwd_varlen(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens,
+                                   section=w.section)
+    a0, a1 = int(w.cu_seqlens[1]), int(w.cu_seqlens[2])
+    k2, v2 = w.k.copy(), w.v.copy()
+    k2[a0:a1] += 3.0
+    v2[a0:a1] -= 7.0
+    out2, _ = ref.oracle_fwd_varlen(w.q, k2, v2, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens,
+                                    section=w.section)
+    keep = np.ones(len(w.q), bool)
+    keep[a0:a1] = False
+    assert np.array_equal(out[keep], out2[keep])
+    assert np.max(np.abs(out[~keep] - out2[~keep])) > 1e-3
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

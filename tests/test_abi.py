@@ -39,8 +39,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_fwd", "mrope_attn_fwd_group",
-        "mrope_attn_group_workspace_size", "mrope_attn_prepare", "mrope_attn_status_string",
-        "mrope_attn_validate", "mrope_attn_workspace_size"])
+        "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size", "mrope_attn_prepare",
+        "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
+        "mrope_attn_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -63,7 +64,7 @@ def test_desc_layout_matches_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 101
+    assert lib.mrope_attn_abi_version() == 102
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -249,3 +250,45 @@ def test_group_rejects_before_launch(lib, monkeypatch):
     monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
     assert _group([d, d], nbytes=need) == -8
     assert _group([d, desc(batch=3, seq=40, text_pad=0)], nbytes=need) == -8
+
+
+# ---------------------------------------------------------------- packed varlen
+def _varlen(d, max_seqlen, cu=FAKE, ws=FAKE, nbytes=1 << 40, lse=None):
+    return B.lib().mrope_attn_fwd_varlen(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu,
+                                         max_seqlen, FAKE, lse, ws, nbytes, None)
+
+
+def test_varlen_workspace(lib):
+    # 3 sequences packed into 9000 tokens, the longest 4608: the table and K'
+    # cover the packed tokens, the tiles 3 x 32 heads x 36 query tiles
+    d = desc(batch=3, seq=9000, heads=32, text_pad=0)
+    tiles = 3 * 32 * 36                       # 3456 = 6 x 512 + 384: no split
+    assert tiles % 512 == 384
+    assert B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(d), 4608) == \
+        9000 * 64 * 8 + 9000 * 32 * 128 * 2
+    # 1 sequence of 4608: 1152 tiles -> 128 split in 2
+    d1 = desc(batch=1, seq=4608, heads=32, text_pad=0)
+    assert B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(d1), 4608) == \
+        B.workspace_size(d1)
+    assert B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(d), 9001) == 0    # > seq
+    assert B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(desc(text_pad=5)), 10) == 0
+    assert B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(d), 0) == 0
+
+
+def test_varlen_rejects_before_launch(lib, monkeypatch):
+    d = desc(batch=3, seq=100, text_pad=0)
+    need = B.lib().mrope_attn_varlen_workspace_size(ctypes.byref(d), 60)
+    assert _varlen(desc(batch=3, seq=100, text_pad=4), 60) == -2
+    assert _varlen(d, 101) == -2
+    assert _varlen(d, -1) == -2
+    assert _varlen(d, 60, cu=None) == -1
+    assert _varlen(d, 60, cu=FAKE + 2) == -5
+    assert _varlen(d, 60, lse=FAKE + 1) == -5
+    assert _varlen(d, 60, nbytes=need - 1) == -7
+    assert _varlen(d, 60, ws=None) == -7
+    assert _varlen(desc(batch=0, seq=100, text_pad=0), 60, cu=None, ws=None, nbytes=0) == 0
+    assert _varlen(d, 0, cu=None, ws=None, nbytes=0) == 0           # nothing to compute
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _varlen(d, 60, nbytes=need) == -8
+    f32 = desc(batch=3, seq=100, text_pad=0, dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))
+    assert _varlen(f32, 60, ws=None, nbytes=0) == -8
