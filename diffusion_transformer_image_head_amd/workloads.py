@@ -39,6 +39,12 @@ CONFIGS = {
                    dtype="bf16", seed=3),
     "long": dict(batch=1, heads=32, head_dim=128, section=(16, 24, 24), text_pad=512,
                  text_lens=None, grid_h=128, grid_w=96, sigma=1.5, dtype="bf16", seed=4),
+    # variants beyond the measured set: 36 heads of 128 (hidden 4608) at
+    # 1024px, and the largest side the pages allow (2048 px -> 128x128 tokens)
+    "h36": dict(batch=1, heads=36, head_dim=128, section=(16, 24, 24), text_pad=512,
+                text_lens=None, grid_h=64, grid_w=64, sigma=1.0, dtype="bf16", seed=5),
+    "2048px": dict(batch=1, heads=32, head_dim=128, section=(16, 24, 24), text_pad=512,
+                   text_lens=None, grid_h=128, grid_w=128, sigma=1.0, dtype="bf16", seed=6),
 }
 
 

@@ -354,7 +354,10 @@ def pin_page_geometry():
         c = CONFIGS[name]
         assert c["grid_h"] == px // comp and c["grid_w"] == px // comp
         assert c["text_pad"] + c["grid_h"] * c["grid_w"] == {512: 1280, 1024: 4608}[px]
-    # the longest config's grid fits the largest side the pages allow
+    # the largest-side config is exactly the largest side the pages allow
+    c = CONFIGS["2048px"]
+    assert c["grid_h"] * comp == facts["max_side_px"] and c["grid_w"] * comp == facts["max_side_px"]
+    # the longest measured config's grid fits the largest side the pages allow
     c = CONFIGS["long"]
     assert max(c["grid_h"], c["grid_w"]) * comp <= facts["max_side_px"]
     assert min(c["grid_h"], c["grid_w"]) * comp >= facts["min_side_px"]

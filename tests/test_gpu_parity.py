@@ -196,7 +196,7 @@ def test_config_512px_full():
     _full_check(config_workload("512px"))
 
 
-@pytest.mark.parametrize("name", ["1024px", "ragged", "long"])
+@pytest.mark.parametrize("name", ["1024px", "ragged", "long", "h36", "2048px"])
 def test_config_sampled_rows(name):
     say(f"case: {name} config, sampled rows")
     w = config_workload(name)
