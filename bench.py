@@ -167,6 +167,59 @@ def bench_cfg(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_bwd(args):
+    """Backward pass on a configuration: the forward runs once (untimed) for
+    out and lse, then `steps` backward calls are timed. FLOPs: the usual 2.5x
+    the forward's (dV, dP, dQ, dK and the recomputed S: five S^2 D products
+    against the forward's two)."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_attn_bwd
+    from diffusion_transformer_image_head_amd.workloads import config_workload, round_to_bf16
+
+    lib()
+    w = config_workload(args.config)
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    q, k, v = (t(x).to(torch.bfloat16) for x in (w.q, w.k, w.v))
+    pos, gq, gk = t(w.pos), t(w.gamma_q), t(w.gamma_k)
+    sl = None if w.seq_lens is None else t(w.seq_lens)
+    kw = dict(text_pad=w.text_pad, section=w.section)
+    out, lse = mrope_attn(q, k, v, pos, gq, gk, sl, return_lse=True, **kw)
+    do = t(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32))).to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+
+    def step():
+        mrope_attn_bwd(q, k, v, pos, gq, gk, sl, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = 2.5 * w.flops()
+    value = flops / (ms * 1e-3) / 1e12
+    bb, s, h, d = w.shape
+    rec = {
+        "metric": "fused QK-norm+M-RoPE attention backward TFLOP/s (2.5x forward FLOPs)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/dO, U[0.5,1.5) gammas; no dataset or weights)",
+        "config": {"workload": f"{args.config} backward: B={bb} H={h} head_dim={d} tokens={s}"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole backward call (prologues, delta, dk/dv, dq, dgamma)"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +231,8 @@ def main():
                          "image-only unconditional pass in one grouped call")
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (dq, dk, dv, dgammas) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -191,6 +246,9 @@ def main():
 
     if args.config == "cfg1024":
         bench_cfg(args)
+        return
+    if args.backward:
+        bench_bwd(args)
         return
 
     import numpy as np

@@ -84,6 +84,11 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_fwd_varlen.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p,
                                             ctypes.c_int32, vp, f32p, vp, ctypes.c_size_t, vp]
         L.mrope_attn_fwd_varlen.restype = ctypes.c_int
+        L.mrope_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(Desc)]
+        L.mrope_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.mrope_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp, f32p,
+                                     vp, vp, vp, vp, f32p, f32p, vp, ctypes.c_size_t, vp]
+        L.mrope_attn_bwd.restype = ctypes.c_int
         L.mrope_attn_abi_version.argtypes = []
         L.mrope_attn_abi_version.restype = ctypes.c_int
         _lib = L
@@ -308,3 +313,42 @@ def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: in
     if rc != 0:
         raise MraError(rc, status_string(rc))
     return (out, lse) if return_lse else out
+
+
+def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, text_pad: int,
+                   section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
+                   dq=None, dk=None, dv=None, workspace=None):
+    """Backward of :func:`mrope_attn` (bf16, head_dim 128): gradients of
+    sum(dout * out) given the forward's out and lse. Returns (dq, dk, dv,
+    dgamma_q, dgamma_k); dq/dk/dv take q/k/v's strides, dout out's."""
+    import torch
+
+    desc, out_, _, seq_lens = _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, False,
+                                       text_pad=text_pad, section=section, theta=theta, eps=eps,
+                                       scale=scale, kprologue="auto")
+    if tuple(dout.shape) != tuple(q.shape) or _bsd_strides(dout) != _bsd_strides(out):
+        raise ValueError("dout must have out's shape and strides")
+    b, s, h, d = q.shape
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (b, h, s) or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [B, H, S] log-sum-exp")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t.shape != ref.shape or _bsd_strides(t) != _bsd_strides(ref):
+            raise ValueError(f"{name} must have the strides of its input")
+    dgq = torch.empty(d, dtype=torch.float32, device=q.device)
+    dgk = torch.empty(d, dtype=torch.float32, device=q.device)
+    need = int(lib().mrope_attn_bwd_workspace_size(ctypes.byref(desc)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mrope_attn_bwd(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              pos.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                              None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), dgq.data_ptr(), dgk.data_ptr(),
+                              None if not need else workspace.data_ptr(), need, stream)
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return dq, dk, dv, dgq, dgk

@@ -51,6 +51,7 @@ struct Args {
   float eps;
   float c2;                 // softmax scale * log2(e)
   float scale;
+  float pscale;             // factor applied by k_prologue_kernel before rounding
   Rope rope;
 };
 

@@ -13,8 +13,8 @@
 
 namespace mra {
 
-// K' = bf16(rope(rmsnorm(K))) into [B, H, S, D], plus the (cos, sin) table
-// [B, S, D/2]. One wave per token; 16 lanes
+// K' = bf16(pscale * rope(rmsnorm(K))) into [B, H, S, D], plus (when a.cs is
+// set) the (cos, sin) table [B, S, D/2]. One wave per token; 16 lanes
 // per head row, so a wave covers 4 heads per step. The token's rotary angles
 // are shared by all heads and computed once per lane with the accurate sincosf.
 template <int D>
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
     g1[p] = a.gk[j];
     g2[p] = a.gk[j + HALF];
     // the same rotation feeds the Q side inside the attention kernel
-    if (hq == 0) a.cs[(int64_t)tok * HALF + j] = make_float2(cs[p], sn[p]);
+    if (hq == 0 && a.cs) a.cs[(int64_t)tok * HALF + j] = make_float2(cs[p], sn[p]);
   }
   const uint16_t* kb = (const uint16_t*)a.k + b * a.ks0 + s * a.ks1;
   for (int h = hq; h < a.H; h += 4) {
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
     ss += __shfl_xor(ss, 2, 16);
     ss += __shfl_xor(ss, 4, 16);
     ss += __shfl_xor(ss, 8, 16);
-    const float r = rsqrtf(ss * (1.0f / D) + a.eps);
+    const float r = rsqrtf(ss * (1.0f / D) + a.eps) * a.pscale;
     uint32_t o1[PPL / 2], o2[PPL / 2];
 #pragma unroll
     for (int p = 0; p < PPL; p += 2) {

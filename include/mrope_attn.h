@@ -200,6 +200,27 @@ int mrope_attn_fwd_varlen(const mra_desc* desc, const void* q, const void* k, co
                           const int32_t* cu_seqlens, int32_t max_seqlen, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Backward pass ---------------------------------------------------------
+ *
+ * Gradients for training (LoRA on the attention projections with gradient
+ * checkpointing, as the SimpleTuner quickstart trains the Ideogram 4 DiT): given
+ * the forward's out and lse (mrope_attn_fwd with a non-NULL lse) and the
+ * upstream gradient dout, writes dq, dk, dv (the gradients of sum(dout * out)
+ * w.r.t. q, k, v; zero rows for padded text slots) and, when not NULL,
+ * dgamma_q and dgamma_k ([D] fp32, summed over every valid row and head; the
+ * sum runs in a fixed order, so results are reproducible). bf16 with
+ * head_dim 128 only (else MRA_ERR_UNSUPPORTED). dout has out's strides
+ * (o_stride); dq, dk, dv have q's, k's and v's strides; all four must be
+ * 16-byte aligned and must not overlap the inputs or each other. The packed
+ * (cu_seqlens) layout has no backward here. */
+size_t mrope_attn_bwd_workspace_size(const mra_desc* desc);
+
+int mrope_attn_bwd(const mra_desc* desc, const void* q, const void* k, const void* v,
+                   const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                   const int32_t* seq_lens, const void* out, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text for a status code. */
 const char* mrope_attn_status_string(int status);
 

@@ -38,7 +38,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_fwd", "mrope_attn_fwd_group",
+        "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_bwd",
+        "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
         "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
         "mrope_attn_workspace_size"])
@@ -64,7 +65,7 @@ def test_desc_layout_matches_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 102
+    assert lib.mrope_attn_abi_version() == 103
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -292,3 +293,38 @@ def test_varlen_rejects_before_launch(lib, monkeypatch):
     assert _varlen(d, 60, nbytes=need) == -8
     f32 = desc(batch=3, seq=100, text_pad=0, dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))
     assert _varlen(f32, 60, ws=None, nbytes=0) == -8
+
+
+# ---------------------------------------------------------------- backward
+def _bwd(d, lse=FAKE, dout=FAKE, dq=FAKE, ws=FAKE, nbytes=1 << 40, dg=FAKE):
+    return B.lib().mrope_attn_bwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  lse, dout, dq, FAKE, FAKE, dg, dg, ws, nbytes, None)
+
+
+def test_bwd_workspace(lib):
+    d = desc(batch=1, seq=4608, heads=32, text_pad=512)
+    rows = 4608 * 32
+    n_wg = 32 * 36
+    want = 4608 * 64 * 8 + 2 * rows * 128 * 2 + 2 * rows * 4 + 2 * n_wg * 128 * 4
+    assert B.lib().mrope_attn_bwd_workspace_size(ctypes.byref(d)) == want
+    assert B.lib().mrope_attn_bwd_workspace_size(ctypes.byref(desc(head_dim=64, section=(8, 12, 12)))) == 0
+    assert B.lib().mrope_attn_bwd_workspace_size(ctypes.byref(desc(dtype=B.MRA_FP32))) == 0
+
+
+def test_bwd_rejects_before_launch(lib, monkeypatch):
+    d = desc()
+    need = B.lib().mrope_attn_bwd_workspace_size(ctypes.byref(d))
+    assert _bwd(desc(head_dim=64, section=(8, 12, 12))) == -6
+    assert _bwd(desc(dtype=B.MRA_FP32)) == -6
+    assert _bwd(desc(section=(1, 2, 3))) == -4
+    assert _bwd(d, lse=None) == -1
+    assert _bwd(d, dout=None) == -1
+    assert _bwd(d, dq=None) == -1
+    assert _bwd(d, dq=FAKE + 8) == -5
+    assert _bwd(d, lse=FAKE + 2) == -5
+    assert _bwd(d, nbytes=need - 1) == -7
+    assert _bwd(d, ws=None) == -7
+    assert _bwd(desc(batch=0), lse=None, dout=None, dq=None, ws=None, nbytes=0) == 0
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _bwd(d, nbytes=need) == -8
+    assert _bwd(d, nbytes=need, dg=None) == -8

@@ -55,3 +55,30 @@ def test_peaked_floor_sets_its_bars():
     # the floor alone breaks the config bars, and the peaked bars leave ~1.5x room
     assert ma > CONFIG_BARS[0] and rr > CONFIG_BARS[1]
     assert ma * 1.3 < PEAKED_BARS[0] and rr * 1.3 < PEAKED_BARS[1], (ma, rr)
+
+
+# ---------------------------------------------------------------- backward
+# Backward bars: rel-RMS of each gradient and max-abs relative to the
+# gradient's largest magnitude. The emulated bf16 rounding floor of the
+# kernels (tests/bwd_emul.py) is ~4.5e-3 rel-RMS and ~0.7% relative max-abs.
+BWD_BARS = (2e-2, 1e-2)
+
+
+def bwd_errors(got, ref):
+    d = got - ref
+    scale = float(np.abs(ref).max()) or 1.0
+    rel = float(np.sqrt(np.sum(d * d) / max(float(np.sum(ref * ref)), 1e-300)))
+    return float(np.abs(d).max()) / scale, rel
+
+
+def test_bwd_bars_sit_above_the_rounding_floor():
+    from oracle.backward import oracle_bwd
+    from tests.bwd_emul import emulate
+    w = make_workload(2, 3, 128, (16, 24, 24), 40, 9, 13, text_lens=(17, 40), seed=600)
+    do = round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32))
+    ref = oracle_bwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens, do,
+                     text_pad=w.text_pad, section=w.section)
+    for got, r in zip(emulate(w, do.astype(np.float64)), ref):
+        ma, rr = bwd_errors(got, r)
+        assert ma * 1.5 <= BWD_BARS[0] and rr * 1.5 <= BWD_BARS[1], (ma, rr)
+        assert rr > 1e-3          # the floor is real: the bars are not loose by orders
