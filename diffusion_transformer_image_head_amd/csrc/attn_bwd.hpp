@@ -43,8 +43,8 @@ struct BwdArgs {
   void* dk;                // strides of k
   void* dv;                // strides of v
   const uint16_t* qp;      // Q'' [B, H, S, D]
-  float* dlt;              // D [B, H, S]
-  float* l2;               // lse * log2 e for valid rows, +inf otherwise [B, H, S]
+  float* ld;               // per row (l2, D) [B, H, S, 2]: l2 = lse * log2 e for valid
+                           // rows, +inf otherwise; D = sum_d dO O (0 for invalid rows)
   float* dgq_part;         // [n_wg_q, D] per-workgroup gamma_q partials
   float* dgk_part;         // [n_wg_k, D]
   float* dgq;              // [D] or null
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs g) {
   for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o, 16);
   if (sub == 0) {
     const int64_t i = ((int64_t)b * a.H + h) * a.S + s;
-    g.dlt[i] = valid ? acc : 0.f;
-    g.l2[i] = valid ? a.lse[i] * kLog2e : INFINITY;
+    g.ld[2 * i] = valid ? a.lse[i] * kLog2e : INFINITY;
+    g.ld[2 * i + 1] = valid ? acc : 0.f;
   }
 }
 
@@ -197,15 +197,39 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   constexpr int KC = D / 16, DB = D / 32, BQ = 32, TILEB = BQ * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
+  constexpr int NST = 4;             // pipeline stages: NST - 1 query tiles in flight
+  constexpr int LOADS = 2 * RUNS + 1;  // direct loads per wave per tile
   static_assert(D == 128, "the backward kernels are written for head_dim 128");
+  // Stage p holds Q'' (Qp), dO (Op) and the (l2, D) pairs (Lp) of one query
+  // tile; separate objects so a stage's reads never wait on another's loads.
   __shared__ __attribute__((aligned(1024))) char Q0[TILEB];
   __shared__ __attribute__((aligned(1024))) char Q1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Q2[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Q3[TILEB];
   __shared__ __attribute__((aligned(1024))) char O0[TILEB];
   __shared__ __attribute__((aligned(1024))) char O1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char O2[TILEB];
+  __shared__ __attribute__((aligned(1024))) char O3[TILEB];
+  __shared__ __attribute__((aligned(256))) float L0[2 * BQ];
+  __shared__ __attribute__((aligned(256))) float L1[2 * BQ];
+  __shared__ __attribute__((aligned(256))) float L2[2 * BQ];
+  __shared__ __attribute__((aligned(256))) float L3[2 * BQ];
   // V rows of the workgroup's 128 keys (row = key, chunk c at c ^ (row & 15)):
   // read back as B operands each tile instead of held in registers
   __shared__ __attribute__((aligned(1024))) char Vk[128 * D * 2];
   __shared__ float red[4 * D];
+  auto qb = [&](auto par) -> char* {
+    constexpr int p = decltype(par)::value;
+    if constexpr (p == 0) return Q0; else if constexpr (p == 1) return Q1; else if constexpr (p == 2) return Q2; else return Q3;
+  };
+  auto ob = [&](auto par) -> char* {
+    constexpr int p = decltype(par)::value;
+    if constexpr (p == 0) return O0; else if constexpr (p == 1) return O1; else if constexpr (p == 2) return O2; else return O3;
+  };
+  auto lb = [&](auto par) -> float* {
+    constexpr int p = decltype(par)::value;
+    if constexpr (p == 0) return L0; else if constexpr (p == 1) return L1; else if constexpr (p == 2) return L2; else return L3;
+  };
 
   const Args& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 31, hf = lane >> 5;
@@ -237,13 +261,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   }
 
   // streamed tiles: run j of this wave fills LDS bytes [(wave*RUNS+j)*1024,
-  // +1024) = rows 4*(wave*RUNS+j) + L/16, physical chunk L%16
+  // +1024) = rows 4*(wave*RUNS+j) + L/16, physical chunk L%16; every wave also
+  // loads the tile's 32 (l2, D) pairs (lane L: float L), the same 256 bytes
   const uint16_t* qbase = g.qp + ((int64_t)b * a.H + head) * S * D;
   const uint32_t qnrec = (uint32_t)((int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, qnrec);
   const uint16_t* obase = (const uint16_t*)g.dout + b * g.ds0 + head * g.ds2;
   const uint32_t onrec = (uint32_t)(((int64_t)(S - 1) * g.ds1 + D) * 2);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(obase, onrec);
+  const float* ldbase = g.ld + ((int64_t)b * a.H + head) * S * 2;
+  const uint32_t lnrec = (uint32_t)((int64_t)S * 2 * 4);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(ldbase, lnrec);
   int t_item[RUNS], q_src[RUNS], o_src[RUNS];
 #pragma unroll
   for (int j = 0; j < RUNS; ++j) {
@@ -253,10 +281,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     q_src[j] = (t_item[j] * D + c * 8) * 2;
     o_src[j] = (int)(((int64_t)t_item[j] * g.ds1 + c * 8) * 2);
   }
-  auto issue = [&](int qt, int buf) {
+  auto issue = [&](int qt, auto par) {
     const int n0 = qt * BQ;
-    char* qd = buf ? Q1 : Q0;
-    char* od = buf ? O1 : O0;
+    char* qd = qb(par);
+    char* od = ob(par);
 #pragma unroll
     for (int j = 0; j < RUNS; ++j) {
       const bool ok = tok_ok(n0 + t_item[j]);
@@ -265,7 +293,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_ptr_t)(qd + (wave * RUNS + j) * 1024), 16, oq, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ors, (lds_ptr_t)(od + (wave * RUNS + j) * 1024), 16, oo, 0, 0, 0);
     }
+    // rows past the end read as (0, 0): their Q'' and dO rows are zero too,
+    // so they add nothing
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_ptr_t)lb(par), 4, (uint32_t)((n0 * 2 + lane) * 4), 0, 0, 0);
   };
+  // wait until at most n tiles' loads of this wave are in flight
+  auto wait_tiles = [&](int n) {
+    if (n >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * LOADS));
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  static_assert(2 * LOADS < 16 && NST - 2 == 2, "vmcnt immediates below");
 
   const int nq = (S + BQ - 1) / BQ;
   auto skipped = [&](int qt) { const int n0 = qt * BQ; return n0 >= L && min(n0 + BQ, S) <= T; };
@@ -281,8 +319,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   const int vg = lane >> 4, vj = lane & 15;
   const int t_key0 = (vg >> 1) * 16 + (vj >> 2);
   const int t_dim0 = 16 * (vg & 1) + 4 * (vj & 3);
-  const float* l2row = g.l2 + ((int64_t)b * a.H + head) * S;
-  const float* dlrow = g.dlt + ((int64_t)b * a.H + head) * S;
 
   // a workgroup whose 128 keys are all padding (or past the end) has zero
   // dk and dv
@@ -291,32 +327,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   int qt = 0;
   while (qt < nq && skipped(qt)) ++qt;
   if (all_pad) qt = nq;
-  if (qt < nq) issue(qt, 0);
+  // prologue: the first NST - 1 tiles into stages 0 .. NST - 2
+  int last = qt, ahead = 0;  // last tile issued; tiles issued after qt
+  if (qt < nq) {
+    issue(qt, Parity<0>{});
+    int t1 = next_q(qt);
+    if (t1 < nq) { issue(t1, Parity<1>{}); last = t1; ++ahead; }
+    int t2 = t1 < nq ? next_q(t1) : nq;
+    if (t2 < nq) { issue(t2, Parity<2>{}); last = t2; ++ahead; }
+  }
 
+  // tile qt sits in stage `parity`; the tile issued here goes to the stage
+  // the previous tile used
   auto step = [&](auto parity) {
     constexpr int cur = decltype(parity)::value;
-    const int qn = next_q(qt);
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_tiles(ahead);
     __syncthreads();
-    if (qn < nq) issue(qn, cur ^ 1);
-    const char* qs = cur ? Q1 : Q0;
-    const char* os = cur ? O1 : O0;
-    const int n0 = qt * BQ;
+    const int tn = last < nq ? next_q(last) : nq;
+    if (tn < nq) { issue(tn, Parity<(cur + NST - 1) % NST>{}); last = tn; ++ahead; }
+    const char* qs = qb(parity);
+    const char* os = ob(parity);
+    const float* ls = lb(parity);
     // S2 (queries x keys) = Q'' K'^T; element i of this lane <-> query hf*16 + i
     f32x16 sacc = {};
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(qs + bwd_off(m, 2 * c + hf)), kf[c],
                                                       sacc, 0, 0, 0);
+    // (l2, D) of the lane's 16 queries
+    f32x4 ldv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ldv[e] = *(const f32x4*)(ls + hf * 32 + e * 4);
     __builtin_amdgcn_sched_barrier(0);  // phases in order: bounds the live fragments
     // P rounded once to bf16: the operand of dV and the factor of dS
     bf16x8 pf[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int n = n0 + hf * 16 + i;
-      const float l2v = n < S ? l2row[n] : INFINITY;
-      pf[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[i] - l2v);
-    }
+    for (int i = 0; i < 16; ++i)
+      pf[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[i] - ldv[i >> 1][(i & 1) * 2]);
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P
 #pragma unroll
@@ -343,11 +390,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 dsf[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int n = n0 + hf * 16 + i;
-      const float dl = n < S ? dlrow[n] : 0.f;
-      dsf[i >> 3][i & 7] = (__bf16)((float)pf[i >> 3][i & 7] * (dpacc[i] - dl));
-    }
+    for (int i = 0; i < 16; ++i)
+      dsf[i >> 3][i & 7] = (__bf16)((float)pf[i >> 3][i & 7] * (dpacc[i] - ldv[i >> 1][(i & 1) * 2 + 1]));
     __builtin_amdgcn_sched_barrier(0);
     // dK'^T += Q''^T dS
 #pragma unroll
@@ -363,12 +407,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
         dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dsf[u], dkacc[db], 0, 0, 0);
       }
-    qt = qn;
+    qt = next_q(qt);
+    --ahead;
   };
   while (qt < nq) {
     step(Parity<0>{});
     if (qt >= nq) break;
     step(Parity<1>{});
+    if (qt >= nq) break;
+    step(Parity<2>{});
+    if (qt >= nq) break;
+    step(Parity<3>{});
   }
 
   // dV rows: dims db*32 + (i/4)*8 + hf*4 + i%4 of key `key`
@@ -434,8 +483,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
     }
   }
   const int64_t rowi = ((int64_t)b * a.H + head) * S + qc;
-  const float l2v = qvalid ? g.l2[rowi] : INFINITY;
-  const float dl = qvalid ? g.dlt[rowi] : 0.f;
+  const float l2v = qvalid ? g.ld[2 * rowi] : INFINITY;
+  const float dl = qvalid ? g.ld[2 * rowi + 1] : 0.f;
 
   const uint16_t* kbase = a.kp + ((int64_t)b * a.H + head) * S * D;
   const uint32_t knrec = (uint32_t)((int64_t)S * D * 2);
@@ -550,13 +599,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
   dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)blockIdx.x * D, wave, lane);
 }
 
-// gamma gradient = sum of the workgroup partials, in workgroup order.
+// gamma gradient = sum of the workgroup partials in a fixed order: thread
+// (grp, d) of 8 x D sums partials grp, grp + 8, ... with four interleaved
+// accumulators, then the 8 x 4 sums are added in a fixed order. blockIdx.y
+// picks the gradient (0: gamma_q, 1: gamma_k).
 template <int D>
-__global__ __launch_bounds__(D) void bwd_dgamma_kernel(const float* part, int n, float* out) {
-  const int d = threadIdx.x;
-  float acc = 0.f;
-  for (int i = 0; i < n; ++i) acc += part[(int64_t)i * D + d];
-  out[d] = acc;
+__global__ __launch_bounds__(8 * D) void bwd_dgamma_kernel(const float* part_q, const float* part_k, int n,
+                                                          float* out_q, float* out_k) {
+  __shared__ float red[8][D];
+  const float* part = blockIdx.x ? part_k : part_q;
+  float* out = blockIdx.x ? out_k : out_q;
+  if (!out) return;
+  const int d = threadIdx.x % D, grp = threadIdx.x / D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int i = grp;
+  for (; i + 24 < n; i += 32) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += part[(int64_t)(i + 8 * u) * D + d];
+  }
+  for (int u = 0; i < n; i += 8, ++u) acc[u & 3] += part[(int64_t)i * D + d];
+  red[grp][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (grp == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) t += red[g][d];
+    out[d] = t;
+  }
 }
 
 }  // namespace mra

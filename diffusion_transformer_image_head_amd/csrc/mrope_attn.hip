@@ -499,11 +499,11 @@ int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const
 
 // ---- backward pass ---------------------------------------------------------
 // Workspace: (cos, sin) table [B, S, D/2] float2, K' and Q'' [B, H, S, D] bf16,
-// D and l2 [B, H, S] fp32, then the gamma partials of the dq and dk/dv
+// (l2, D) pairs [B, H, S, 2] fp32, then the gamma partials of the dq and dk/dv
 // workgroups [n_wg, D] fp32 each; every piece 256-byte aligned.
 struct BwdPlan {
   int n_t, n_wg;
-  size_t off_cs, off_kp, off_qp, off_dlt, off_l2, off_gq, off_gk, bytes;
+  size_t off_cs, off_kp, off_qp, off_ld, off_gq, off_gk, bytes;
 };
 
 static BwdPlan bwd_plan(const mra_desc* d) {
@@ -515,8 +515,7 @@ static BwdPlan bwd_plan(const mra_desc* d) {
   p.off_cs = off; off += table_bytes(d);
   p.off_kp = off; off += round_up(rows * d->head_dim * 2, kWsAlign);
   p.off_qp = off; off += round_up(rows * d->head_dim * 2, kWsAlign);
-  p.off_dlt = off; off += round_up(rows * 4, kWsAlign);
-  p.off_l2 = off; off += round_up(rows * 4, kWsAlign);
+  p.off_ld = off; off += round_up(rows * 8, kWsAlign);
   p.off_gq = off; off += round_up((size_t)p.n_wg * d->head_dim * 4, kWsAlign);
   p.off_gk = off; off += round_up((size_t)p.n_wg * d->head_dim * 4, kWsAlign);
   p.bytes = off;
@@ -563,8 +562,7 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   g.ds0 = d->o_stride[0]; g.ds1 = d->o_stride[1]; g.ds2 = d->o_stride[2];
   g.dq = dq; g.dk = dk; g.dv = dv;
   g.qp = (const uint16_t*)(w + p.off_qp);
-  g.dlt = (float*)(w + p.off_dlt);
-  g.l2 = (float*)(w + p.off_l2);
+  g.ld = (float*)(w + p.off_ld);
   g.dgq_part = (float*)(w + p.off_gq);
   g.dgk_part = (float*)(w + p.off_gk);
   g.dgq = dgamma_q; g.dgk = dgamma_k;
@@ -582,8 +580,9 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
   hipLaunchKernelGGL(mra::bwd_dkdv_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
   hipLaunchKernelGGL(mra::bwd_dq_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-  if (dgamma_q) hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(1), dim3(128), 0, s, (const float*)g.dgq_part, p.n_wg, dgamma_q);
-  if (dgamma_k) hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(1), dim3(128), 0, s, (const float*)g.dgk_part, p.n_wg, dgamma_k);
+  if (dgamma_q || dgamma_k)
+    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2), dim3(8 * 128), 0, s, (const float*)g.dgq_part,
+                       (const float*)g.dgk_part, p.n_wg, dgamma_q, dgamma_k);
   return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
