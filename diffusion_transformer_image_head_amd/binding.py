@@ -42,6 +42,21 @@ class Problem(ctypes.Structure):
 MAX_GROUP = 4
 
 
+class QkvDesc(ctypes.Structure):
+    """Mirror of ``mra_qkv_desc`` (include/mrope_attn.h)."""
+    _fields_ = [
+        ("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("section", ctypes.c_int32 * 3),
+        ("theta", ctypes.c_float), ("eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+        ("x_stride", ctypes.c_int64), ("q_stride", ctypes.c_int64 * 2),
+        ("k_stride", ctypes.c_int64 * 2), ("v_stride", ctypes.c_int64 * 2),
+    ]
+
+
+KPRO_NONE = 3
+_KPRO["none"] = KPRO_NONE
+
+
 class MraError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"mrope_attn status {status}: {msg}")
@@ -89,6 +104,11 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp, f32p,
                                      vp, vp, vp, vp, f32p, f32p, vp, ctypes.c_size_t, vp]
         L.mrope_attn_bwd.restype = ctypes.c_int
+        L.mrope_qkv_proj_workspace_size.argtypes = [ctypes.POINTER(QkvDesc)]
+        L.mrope_qkv_proj_workspace_size.restype = ctypes.c_size_t
+        L.mrope_qkv_proj.argtypes = [ctypes.POINTER(QkvDesc), vp, vp, f32p, i32p, f32p, f32p, vp, vp, vp,
+                                     vp, ctypes.c_size_t, vp]
+        L.mrope_qkv_proj.restype = ctypes.c_int
         L.mrope_attn_abi_version.argtypes = []
         L.mrope_attn_abi_version.restype = ctypes.c_int
         _lib = L
@@ -137,8 +157,11 @@ def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_
     """Shape/dtype/device checks; returns (desc, out, lse, seq_lens)."""
     import torch
 
+    given = kprologue in ("none", KPRO_NONE)
     for name, t in (("q", q), ("k", k), ("v", v), ("pos", pos), ("gamma_q", gamma_q),
                     ("gamma_k", gamma_k)):
+        if t is None and given and name in ("pos", "gamma_q", "gamma_k"):
+            continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
     if q.dtype == torch.bfloat16:
@@ -152,10 +175,11 @@ def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_
     b, s, h, d = q.shape
     if tuple(k.shape) != (b, s, h, d) or tuple(v.shape) != (b, s, h, d):
         raise ValueError("q, k, v shapes differ")
-    if pos.dtype != torch.int32 or tuple(pos.shape) != (b, s, 3) or not pos.is_contiguous():
+    if pos is not None and (pos.dtype != torch.int32 or tuple(pos.shape) != (b, s, 3)
+                            or not pos.is_contiguous()):
         raise ValueError("pos must be contiguous int32 [B, S, 3]")
     for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
-        if g.dtype != torch.float32 or tuple(g.shape) != (d,) or not g.is_contiguous():
+        if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != (d,) or not g.is_contiguous()):
             raise ValueError(f"{name} must be contiguous float32 [D]")
     if seq_lens is not None:
         if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (b,) or not seq_lens.is_cuda:
@@ -194,13 +218,15 @@ def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     ws = None if not need else workspace.data_ptr()
     if stage in ("fwd", "attend"):
         fn = lib().mrope_attn_fwd if stage == "fwd" else lib().mrope_attn_attend
-        rc = fn(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), pos.data_ptr(),
-                gamma_q.data_ptr(), gamma_k.data_ptr(),
+        ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        rc = fn(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr(pos),
+                ptr(gamma_q), ptr(gamma_k),
                 None if seq_lens is None else seq_lens.data_ptr(), out.data_ptr(),
                 None if lse is None else lse.data_ptr(), ws, need, stream)
     elif stage == "prepare":
-        rc = lib().mrope_attn_prepare(ctypes.byref(desc), k.data_ptr(), pos.data_ptr(),
-                                      gamma_k.data_ptr(), ws, need, stream)
+        rc = lib().mrope_attn_prepare(ctypes.byref(desc), k.data_ptr(),
+                                      None if pos is None else pos.data_ptr(),
+                                      None if gamma_k is None else gamma_k.data_ptr(), ws, need, stream)
     else:
         raise ValueError(f"unknown stage {stage}")
     if rc != 0:
@@ -352,3 +378,59 @@ def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, 
     if rc != 0:
         raise MraError(rc, status_string(rc))
     return dq, dk, dv, dgq, dgk
+
+
+def make_qkv_desc(tokens, hidden, heads, head_dim=128, *, section=(16, 24, 24), theta=10000.0,
+                  eps=1e-6, scale=None, x_stride=None, q_stride=None, k_stride=None,
+                  v_stride=None) -> QkvDesc:
+    d = QkvDesc()
+    d.tokens, d.hidden, d.heads, d.head_dim = tokens, hidden, heads, head_dim
+    d.section[:] = [int(x) for x in section]
+    d.theta, d.eps = float(theta), float(eps)
+    d.softmax_scale = 0.0 if scale is None else float(scale)
+    d.x_stride = hidden if x_stride is None else int(x_stride)
+    cont = (heads * head_dim, head_dim)
+    for name, st in (("q_stride", q_stride), ("k_stride", k_stride), ("v_stride", v_stride)):
+        getattr(d, name)[:] = list(cont if st is None else st)
+    return d
+
+
+def mrope_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, section=(16, 24, 24),
+                   theta: float = 10000.0, eps: float = 1e-6, scale=None, out=None, workspace=None):
+    """fp8 e4m3 QKV projection with the norm/rotation epilogue.
+
+    x [M, hidden] bf16, w8 [3 H D, hidden] uint8 (e4m3 codes), w_scale [3 H D]
+    fp32, pos [M, 3] int32, gammas [D] fp32. Returns (q_op, k_op, v), each
+    [M, H, D] bf16: the operands mrope_attn takes with kprologue="none"."""
+    import torch
+
+    for name, t in (("x", x), ("w8", w8), ("w_scale", w_scale), ("pos", pos), ("gamma_q", gamma_q),
+                    ("gamma_k", gamma_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [M, hidden] with contiguous rows")
+    m, hidden = x.shape
+    d = gamma_q.numel()
+    if w8.dtype != torch.uint8 or tuple(w8.shape) != (3 * heads * d, hidden) or not w8.is_contiguous():
+        raise ValueError("w8 must be contiguous uint8 [3 H D, hidden]")
+    if w_scale.dtype != torch.float32 or w_scale.numel() != 3 * heads * d or not w_scale.is_contiguous():
+        raise ValueError("w_scale must be contiguous float32 [3 H D]")
+    if pos.dtype != torch.int32 or tuple(pos.shape) != (m, 3) or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32 [M, 3]")
+    if out is None:
+        out = tuple(torch.empty((m, heads, d), dtype=torch.bfloat16, device=x.device) for _ in range(3))
+    st = [(t.stride(0), t.stride(1)) for t in out]
+    desc = make_qkv_desc(m, hidden, heads, d, section=section, theta=theta, eps=eps, scale=scale,
+                         x_stride=x.stride(0), q_stride=st[0], k_stride=st[1], v_stride=st[2])
+    need = int(lib().mrope_qkv_proj_workspace_size(ctypes.byref(desc)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib().mrope_qkv_proj(ctypes.byref(desc), x.data_ptr(), w8.data_ptr(), w_scale.data_ptr(),
+                              pos.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(), out[0].data_ptr(),
+                              out[1].data_ptr(), out[2].data_ptr(),
+                              None if not need else workspace.data_ptr(), need, stream)
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return out

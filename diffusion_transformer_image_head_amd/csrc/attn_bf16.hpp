@@ -102,8 +102,12 @@ __device__ __forceinline__ float* part_record(float* part, int nsplit, int st, i
   return part + (((int64_t)st * nsplit + p) * (WAVES * RB) + rr) * REC;
 }
 
-template <int D, int WAVES, int BN, int RB, bool KFUSED, int G>
+// KPM: where Q' and K' come from. 0: K' from the prepass in the workspace,
+// Q' made here from q; 1: both made here (K while its tile is staged);
+// 2: q and k already hold the operands Q'' (scaled by c2) and K'.
+template <int D, int WAVES, int BN, int RB, int KPM, int G>
 __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Group<G> gp) {
+  constexpr bool KFUSED = KPM == 1, PRE = KPM == 2;
   constexpr int BM = WAVES * 32 * RB;
   constexpr int NT = WAVES * 64;
   constexpr int KC = D / 16;                 // 16-wide head_dim chunks (QK^T k-steps)
@@ -186,6 +190,19 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   // one bf16 rounding, kept as the B operand of S^T: lane (m, hf) holds
   // Q'[row][c*16 + hf*8 + e].
   bf16x8 qf[RB][KC];
+  if constexpr (PRE) {
+    // the operand as given: rows past the end read as zeros
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint16_t* src = (const uint16_t*)a.q + bl * a.qs0 + (tok0 + min(row[rb], S - 1)) * a.qs1 + head * a.qs2;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const u32x4 w = *(const u32x4*)(src + c * 16 + hf * 8);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        qf[rb][c] = __builtin_bit_cast(bf16x8, in_seq[rb] ? w : z);
+      }
+    }
+  } else
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float x[KC][8];
@@ -254,8 +271,8 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
 
   // ---- operand sources. All bounds live in the per-lane offset: a row that
   // must not be read gets an offset at the resource size, which reads zeros.
-  const int64_t krow = KFUSED ? a.ks1 : D;  // elements between K rows
-  const uint16_t* kbase = KFUSED ? (const uint16_t*)a.k + bl * a.ks0 + tok0 * a.ks1 + head * a.ks2
+  const int64_t krow = (KFUSED || PRE) ? a.ks1 : D;  // elements between K rows
+  const uint16_t* kbase = (KFUSED || PRE) ? (const uint16_t*)a.k + bl * a.ks0 + tok0 * a.ks1 + head * a.ks2
                                  : a.kp + (((int64_t)bl * a.H + head) * Sx + tok0) * D;
   const uint32_t knrec = (uint32_t)(((int64_t)(S - 1) * krow + D) * 2);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, knrec);

@@ -9,6 +9,7 @@
 #include "mrope_attn.h"
 #include "attn_bf16.hpp"
 #include "attn_bwd.hpp"
+#include "qkv_proj.hpp"
 #include "attn_fp32.hpp"
 #include "prologue.hpp"
 
@@ -63,7 +64,7 @@ int check_desc(const mra_desc* d) {
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
   if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
   if (d->dtype == MRA_BF16 && d->kprologue != MRA_KPRO_AUTO && d->kprologue != MRA_KPRO_FUSED &&
-      d->kprologue != MRA_KPRO_PREPASS)
+      d->kprologue != MRA_KPRO_PREPASS && d->kprologue != MRA_KPRO_NONE)
     return MRA_ERR_PARAM;
   return MRA_OK;
 }
@@ -94,6 +95,7 @@ struct Plan {
 };
 
 size_t table_bytes(const mra_desc* d) {
+  if (d->dtype == MRA_BF16 && resolve_kprologue(d) == MRA_KPRO_NONE) return 0;
   return round_up((size_t)d->batch * d->seq * (d->head_dim / 2) * sizeof(float2), kWsAlign);
 }
 size_t kprime_bytes(const mra_desc* d) {
@@ -169,7 +171,7 @@ void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const v
 // Points problem j's Args at its pieces of the workspace.
 void bind_workspace(Args& a, const mra_desc* d, const Plan& p, int j, void* workspace) {
   char* w = (char*)workspace;
-  a.cs = (float2*)(w + p.off_table[j]);
+  a.cs = resolve_kprologue(d) == MRA_KPRO_NONE ? nullptr : (float2*)(w + p.off_table[j]);
   a.kp = resolve_kprologue(d) == MRA_KPRO_PREPASS ? (uint16_t*)(w + p.off_kp[j]) : nullptr;
   a.n_qt = p.n_qt[j];
 }
@@ -177,6 +179,7 @@ void bind_workspace(Args& a, const mra_desc* d, const Plan& p, int j, void* work
 template <int D>
 hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
   const int64_t tokens = (int64_t)a.B * a.S;
+  if (kpro == MRA_KPRO_NONE) return hipSuccess;  // the operands are given
   if (kpro == MRA_KPRO_PREPASS) {
     hipLaunchKernelGGL(mra::k_prologue_kernel<D>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, a);
   } else {
@@ -190,9 +193,11 @@ template <int D, int G>
 hipError_t launch_attend_group(const mra::Group<G>& g, int kpro, hipStream_t s) {
   const unsigned grid = (unsigned)(g.n_whole + g.n_split * g.nsplit);
   if (kpro == MRA_KPRO_PREPASS)
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, false, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 0, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+  else if (kpro == MRA_KPRO_FUSED)
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 1, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
   else
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, true, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 2, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
   if (g.n_split) {
     const int64_t threads = (int64_t)g.n_split * kWaves * kRowBlocks * (D / 8) * 64;
     hipLaunchKernelGGL((mra::split_merge_kernel<D, kWaves, kRowBlocks, G>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, g);
@@ -242,7 +247,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 103; }
+int mrope_attn_abi_version(void) { return 104; }
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {
@@ -267,7 +272,9 @@ int mrope_attn_validate(const mra_desc* d, const void* q, const void* k, const v
   int rc = check_desc(d);
   if (rc != MRA_OK) return rc;
   if (d->batch == 0 || d->seq == 0) return MRA_OK;
-  if (!q || !k || !v || !pos || !gq || !gk || !out) return MRA_ERR_NULL;
+  // operands given (MRA_KPRO_NONE): positions and gammas are not read
+  const bool given = d->dtype == MRA_BF16 && d->kprologue == MRA_KPRO_NONE;
+  if (!q || !k || !v || !out || (!given && (!pos || !gq || !gk))) return MRA_ERR_NULL;
   if ((rc = check_strides(d->q_stride, d->dtype)) != MRA_OK) return rc;
   if ((rc = check_strides(d->k_stride, d->dtype)) != MRA_OK) return rc;
   if ((rc = check_strides(d->v_stride, d->dtype)) != MRA_OK) return rc;
@@ -526,6 +533,7 @@ static int bwd_check(const mra_desc* d) {
   int rc = check_desc(d);
   if (rc != MRA_OK) return rc;
   if (d->dtype != MRA_BF16 || d->head_dim != 128) return MRA_ERR_UNSUPPORTED;
+  if (d->kprologue == MRA_KPRO_NONE) return MRA_ERR_UNSUPPORTED;
   return MRA_OK;
 }
 
@@ -583,6 +591,87 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   if (dgamma_q || dgamma_k)
     hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2), dim3(8 * 128), 0, s, (const float*)g.dgq_part,
                        (const float*)g.dgk_part, p.n_wg, dgamma_q, dgamma_k);
+  return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+// ---- fp8 QKV projection --------------------------------------------------
+static int qkv_check(const mra_qkv_desc* d) {
+  if (!d) return MRA_ERR_NULL;
+  if (d->tokens < 0 || d->heads < 1 || d->hidden <= 0 || d->hidden % 64 != 0) return MRA_ERR_SHAPE;
+  if (d->head_dim != 128) return MRA_ERR_UNSUPPORTED;
+  if (d->section[0] < 0 || d->section[1] < 0 || d->section[2] < 0 ||
+      (int64_t)d->section[0] + d->section[1] + d->section[2] != d->head_dim / 2)
+    return MRA_ERR_SECTION;
+  if (!(d->theta > 0.f) || !std::isfinite(d->theta)) return MRA_ERR_PARAM;
+  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
+  if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
+  if (d->x_stride < d->hidden || d->x_stride % 8 != 0) return MRA_ERR_STRIDE;
+  const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
+  for (int i = 0; i < 3; ++i)
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][0] % 8 != 0 || st[i][1] % 8 != 0) return MRA_ERR_STRIDE;
+  // 32-bit byte offsets inside x and each weight block
+  if ((int64_t)d->tokens * d->x_stride * 2 >= ((int64_t)1 << 31)) return MRA_ERR_UNSUPPORTED;
+  if ((int64_t)d->head_dim * d->hidden >= ((int64_t)1 << 31)) return MRA_ERR_UNSUPPORTED;
+  return MRA_OK;
+}
+
+size_t mrope_qkv_proj_workspace_size(const mra_qkv_desc* d) {
+  if (qkv_check(d) != MRA_OK || d->tokens == 0) return 0;
+  return round_up((size_t)d->tokens * (d->head_dim / 2) * sizeof(float2), kWsAlign);
+}
+
+int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, const float* w_scale,
+                   const int32_t* pos, const float* gq, const float* gk, void* q_out, void* k_out,
+                   void* v_out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = qkv_check(d);
+  if (rc != MRA_OK) return rc;
+  if (d->tokens == 0) return MRA_OK;
+  if (!x || !w8 || !w_scale || !pos || !gq || !gk || !q_out || !k_out || !v_out) return MRA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w8, 16) || !aligned(w_scale, 16) || !aligned(gq, 16) ||
+      !aligned(gk, 16) || !aligned(pos, 4) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
+      !aligned(v_out, 16))
+    return MRA_ERR_STRIDE;
+  const size_t need = mrope_qkv_proj_workspace_size(d);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+
+  // the rotary table of the tokens, from the same kernel the attention uses
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.pos = pos;
+  a.B = 1;
+  a.S = d->tokens;
+  a.cs = (float2*)workspace;
+  const int half = d->head_dim / 2;
+  for (int j = 0; j < half; ++j)
+    a.rope.inv_freq[j] = (float)std::pow((double)d->theta, -2.0 * j / d->head_dim);
+  a.rope.sec_t = d->section[0];
+  a.rope.sec_th = d->section[0] + d->section[1];
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n = (int64_t)d->tokens * half;
+  hipLaunchKernelGGL(mra::rope_table_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+
+  mra::QkvArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.x = (const uint16_t*)x;
+  g.xs = d->x_stride;
+  g.w8 = w8;
+  g.wsc = w_scale;
+  g.cs = (const float2*)workspace;
+  g.gq = gq;
+  g.gk = gk;
+  g.out[0] = (uint16_t*)q_out; g.out[1] = (uint16_t*)k_out; g.out[2] = (uint16_t*)v_out;
+  const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
+  for (int i = 0; i < 3; ++i) { g.os[i][0] = st[i][0]; g.os[i][1] = st[i][1]; }
+  g.M = d->tokens;
+  g.hidden = d->hidden;
+  g.H = d->heads;
+  g.n_mt = (d->tokens + 255) / 256;
+  g.eps = d->eps;
+  const float scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  g.qscale = (float)((double)scale * 1.4426950408889634);
+  hipLaunchKernelGGL(mra::qkv_proj_kernel<128>, dim3((unsigned)(g.n_mt * 3 * d->heads)), dim3(256), 0, s, g);
   return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

@@ -1,0 +1,212 @@
+// fp8 e4m3 QKV projection with the QK-RMSNorm + 3D M-RoPE epilogue (gfx950).
+//
+// The checkpoint stores the fused qkv weight [3 * H * D, hidden] (Q, K, V rows
+// stacked) as float8 e4m3 with one scale per output row; the real weight is
+// the fp8 value times its row's scale (unsloth commit log for the Ideogram 4
+// backend). The projection feeds the attention's QK-RMSNorm and 3D M-RoPE
+// (Ideogram 4.0 announcement thread), so its epilogue produces the attention's
+// operands directly:
+//   q_op = bf16(qscale * rope(rmsnorm(x Wq^T) * gamma_q)),
+//   k_op = bf16(rope(rmsnorm(x Wk^T) * gamma_k)),  v = bf16(x Wv^T).
+//
+// One workgroup per (256 tokens, one head of Q, K or V = 128 output rows),
+// 4 waves of 64 tokens. Output transposed on the matrix cores:
+// C^T (rows x tokens) = W x^T with v_mfma_f32_32x32x16_bf16, A = W rows read
+// from LDS, B = the wave's x rows loaded straight into registers (each wave
+// owns its tokens). Each 64-wide hidden chunk of W arrives as fp8 by direct
+// loads into LDS (double-buffered), is widened once to bf16 in LDS by the
+// whole workgroup (v_cvt_scalef32_pk_bf16_fp8: exact for e4m3) and read by the
+// four waves; the row scale factors out of the sum and is applied in the
+// epilogue. A lane pair then holds all 128 rows of one token, so the RMSNorm
+// is lane-local plus one swap and each rotary pair (j, j + 64) sits in one
+// lane.
+#pragma once
+
+#include "attn_bf16.hpp"
+
+namespace mra {
+
+struct QkvArgs {
+  const uint16_t* x;      // [M, hidden] bf16, row stride xs
+  int64_t xs;
+  const uint8_t* w8;      // [3 H D, hidden] e4m3
+  const float* wsc;       // [3 H D]
+  const float2* cs;       // (cos, sin) [M, D/2]
+  const float* gq;
+  const float* gk;
+  uint16_t* out[3];       // q_op, k_op, v: [M, H, D] with (token, head) strides
+  int64_t os[3][2];
+  int32_t M, hidden, H, n_mt;
+  float eps, qscale;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void qkv_proj_kernel(QkvArgs g) {
+  constexpr int KB = 64;              // hidden chunk
+  constexpr int W8B = D * KB;         // fp8 chunk bytes (8 KB)
+  constexpr int DB = D / 32, KS = KB / 16;
+  static_assert(D == 128, "written for head_dim 128");
+  __shared__ __attribute__((aligned(1024))) uint8_t W0[W8B];
+  __shared__ __attribute__((aligned(1024))) uint8_t W1[W8B];
+  __shared__ __attribute__((aligned(1024))) char Wb[D * KB * 2];   // bf16, 128-byte rows
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 31, hf = lane >> 5;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = tile % g.n_mt, hb = tile / g.n_mt;     // hb in [0, 3H)
+  const int part = hb / g.H, head = hb % g.H;
+  const int t0 = mt * 256 + wave * 64;
+
+  // x rows of this lane's two tokens: buffer loads, rows past M read zeros
+  const uint32_t xnrec = (uint32_t)((int64_t)g.M * g.xs * 2);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.x, xnrec);
+  uint32_t xoff[2];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int tok = t0 + tb * 32 + m;
+    xoff[tb] = tok < g.M ? (uint32_t)(((int64_t)tok * g.xs + hf * 8) * 2) : xnrec;
+  }
+  auto load_x = [&](int kc, u32x4 (&xf)[2][KS]) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        xf[tb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+            xrs, xoff[tb] == xnrec ? xnrec : xoff[tb] + (uint32_t)((kc * KB + ks * 16) * 2), 0, 0);
+  };
+  // W chunk: run j of this wave = bytes [(wave*2+j)*1024, +1024) = rows
+  // (wave*2+j)*16 + L/4, bytes (L%4)*16 of the row
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(g.w8 + (int64_t)hb * D * g.hidden, (uint32_t)(D * g.hidden));
+  uint32_t woff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (wave * 2 + j) * 16 + (lane >> 2);
+    woff[j] = (uint32_t)(row * g.hidden + (lane & 3) * 16);
+  }
+  auto issue_w = [&](int kc, uint8_t* dst) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(dst + (wave * 2 + j) * 1024), 16,
+                                               woff[j] + kc * KB, 0, 0, 0);
+  };
+  // widen the fp8 chunk to bf16: thread t converts row t/2, bytes (t%2)*32..+31
+  // into logical chunks (t%2)*4 .. +3 of the bf16 row (chunk c at c ^ swz(row))
+  auto widen = [&](const uint8_t* src) {
+    const int row = tid >> 1, h = tid & 1;
+    const u32x4 a = *(const u32x4*)(src + row * KB + h * 32);
+    const u32x4 b = *(const u32x4*)(src + row * KB + h * 32 + 16);
+    const uint32_t wv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const int swz = (row >> 1) & 7;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t w = wv[2 * c + e];
+        o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+        o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+      }
+      *(u32x4*)(Wb + row * (KB * 2) + (((h * 4 + c) ^ swz) << 4)) = o;
+    }
+  };
+
+  f32x16 acc[2][DB];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tb][db][i] = 0.f;
+
+  const int nk = g.hidden / KB;
+  u32x4 xf[2][KS], xn[2][KS];
+  issue_w(0, W0);
+  load_x(0, xn);
+  auto step = [&](int kc, auto parity) {
+    constexpr int cur = decltype(parity)::value;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // W8(kc) landed; every wave is done with Wb
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) xf[tb][ks] = xn[tb][ks];
+    if (kc + 1 < nk) {
+      issue_w(kc + 1, cur ? W0 : W1);
+      load_x(kc + 1, xn);
+    }
+    widen(cur ? W1 : W0);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int row = db * 32 + m;
+        const bf16x8 a = *(const bf16x8*)(Wb + row * (KB * 2) + (((2 * ks + hf) ^ ((row >> 1) & 7)) << 4));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          acc[tb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, xf[tb][ks]),
+                                                                acc[tb][db], 0, 0, 0);
+      }
+  };
+  for (int kc = 0; kc < nk; kc += 2) {
+    step(kc, Parity<0>{});
+    if (kc + 1 < nk) step(kc + 1, Parity<1>{});
+  }
+
+  // ---- epilogue: row scale; Q/K heads: RMSNorm, gamma, rotation (Q: qscale)
+  const float* wsc = g.wsc + hb * D;
+  const float* gamma = part == 0 ? g.gq : g.gk;
+  const float qs = part == 0 ? g.qscale : 1.0f;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int tok = t0 + tb * 32 + m;
+    float y[DB][16];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const f32x4 sc = *(const f32x4*)(wsc + db * 32 + gg * 8 + hf * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[db][gg * 4 + e] = acc[tb][db][gg * 4 + e] * sc[e];
+      }
+    if (part < 2) {
+      float ss = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += y[db][i] * y[db][i];
+      ss = half_swap_sum(ss);
+      const float r = rsqrtf(ss * (1.0f / D) + g.eps);
+      const float2* csrow = g.cs + (int64_t)min(tok, g.M - 1) * (D / 2);
+#pragma unroll
+      for (int db = 0; db < DB / 2; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int j0 = db * 32 + gg * 8 + hf * 4;
+          const f32x4 c01 = *(const f32x4*)(csrow + j0);
+          const f32x4 c23 = *(const f32x4*)(csrow + j0 + 2);
+          const f32x4 g1 = *(const f32x4*)(gamma + j0);
+          const f32x4 g2 = *(const f32x4*)(gamma + j0 + D / 2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float cs = e < 2 ? c01[2 * e] : c23[2 * (e - 2)];
+            const float sn = e < 2 ? c01[2 * e + 1] : c23[2 * (e - 2) + 1];
+            const float u = y[db][gg * 4 + e] * r * g1[e];
+            const float w = y[db + DB / 2][gg * 4 + e] * r * g2[e];
+            y[db][gg * 4 + e] = (u * cs - w * sn) * qs;
+            y[db + DB / 2][gg * 4 + e] = (w * cs + u * sn) * qs;
+          }
+        }
+    }
+    if (tok < g.M) {
+      uint16_t* dst = g.out[part] + (int64_t)tok * g.os[part][0] + (int64_t)head * g.os[part][1];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          *(u32x2*)(dst + db * 32 + gg * 8 + hf * 4) =
+              u32x2{pack_bf16(y[db][gg * 4], y[db][gg * 4 + 1]), pack_bf16(y[db][gg * 4 + 2], y[db][gg * 4 + 3])};
+    }
+  }
+}
+
+}  // namespace mra

@@ -178,3 +178,47 @@ def make_varlen_workload(heads, head_dim, section, text_lens, grids, sigma=1.0, 
     return VarlenWorkload(q=cat("q"), k=cat("k"), v=cat("v"), pos=cat("pos"),
                           gamma_q=parts[0].gamma_q, gamma_k=parts[0].gamma_k, cu_seqlens=cu,
                           section=tuple(section), dtype=dtype)
+
+
+@dataclass
+class QkvWorkload:
+    """Inputs of the fp8 QKV projection for a [batch, text_pad + image]
+    layout: x [B*S, hidden] (bf16-exact), w8 [3 H D, hidden] e4m3 codes,
+    w_scale [3 H D], pos [B*S, 3]."""
+    x: np.ndarray
+    w8: np.ndarray
+    w_scale: np.ndarray
+    pos: np.ndarray
+    gamma_q: np.ndarray
+    gamma_k: np.ndarray
+    batch: int
+    seq: int
+    heads: int
+    head_dim: int
+    text_pad: int
+    section: tuple
+
+    def flops(self):
+        return 2 * self.x.shape[0] * self.x.shape[1] * self.w8.shape[0]
+
+
+def make_qkv_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w, hidden,
+                      seed=0) -> QkvWorkload:
+    """x ~ N(0, 1) rounded to bf16; a dense weight ~ N(0, 1/hidden) quantized
+    per output row to float8 e4m3 (scale = row max / 448, round to nearest via
+    the library's float8_e4m3fn cast), as the checkpoint stores it."""
+    import torch
+    rng = np.random.default_rng(seed)
+    s = text_pad + grid_h * grid_w
+    m = batch * s
+    x = round_to_bf16(rng.standard_normal((m, hidden), dtype=np.float32))
+    n = 3 * heads * head_dim
+    w = rng.standard_normal((n, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden))
+    scale = (np.abs(w).max(axis=1) / 448.0).astype(np.float32)
+    codes = torch.from_numpy(w / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    gq = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    pos = positions(batch, text_pad, grid_h, grid_w).reshape(m, 3)
+    return QkvWorkload(x=x, w8=np.ascontiguousarray(codes), w_scale=scale, pos=np.ascontiguousarray(pos),
+                       gamma_q=gq, gamma_k=gk, batch=batch, seq=s, heads=heads, head_dim=head_dim,
+                       text_pad=text_pad, section=tuple(section))

@@ -77,7 +77,11 @@ typedef enum { MRA_BF16 = 0, MRA_FP32 = 1 } mra_dtype;
 typedef enum {
   MRA_KPRO_AUTO = 0,    /* library's choice (currently MRA_KPRO_PREPASS) */
   MRA_KPRO_FUSED = 1,   /* applied while each K tile is staged into LDS */
-  MRA_KPRO_PREPASS = 2  /* one pass writes K' (bf16) to the workspace first */
+  MRA_KPRO_PREPASS = 2, /* one pass writes K' (bf16) to the workspace first */
+  MRA_KPRO_NONE = 3     /* q and k already hold the operands Q'' and K' (as written
+                           by mrope_qkv_proj with the same softmax_scale): no norm
+                           or rotation is applied; pos_thw, gamma_q, gamma_k are
+                           not read and may be NULL */
 } mra_kprologue;
 
 typedef struct {
@@ -220,6 +224,45 @@ int mrope_attn_bwd(const mra_desc* desc, const void* q, const void* k, const voi
                    const int32_t* seq_lens, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- fp8 QKV projection with the norm/rotation epilogue ------------------
+ *
+ * The checkpoint's attention projection is one fused weight [3 * H * D, hidden]
+ * with the Q, K and V rows stacked, stored as float8 e4m3 (OCP E4M3, the
+ * float8_e4m3fn type) with one fp32 scale per output row: the real weight is
+ * fp8 value * scale (unsloth commit log for the Ideogram 4 backend, the fp8
+ * loader commit). mrope_qkv_proj computes y = x W^T for bf16 activations x
+ * [tokens, hidden] (fp32 accumulation, the row scale applied to the sums) and
+ * writes the attention's operands:
+ *   q_out = bf16(softmax_scale * log2(e) * rope(rmsnorm(y_q) * gamma_q))  (Q'')
+ *   k_out = bf16(rope(rmsnorm(y_k) * gamma_k))                            (K')
+ *   v_out = bf16(y_v)
+ * per head, with the rotation and norm of mrope_attn_fwd (pos_thw [tokens, 3]).
+ * Feed them to mrope_attn_fwd with kprologue = MRA_KPRO_NONE and the same
+ * softmax_scale. head_dim 128 only; hidden a positive multiple of 64.
+ * Outputs are [tokens, H, D] views with the given token and head strides
+ * (multiples of 8 elements, 16-byte aligned bases, no overlap). */
+typedef struct {
+  int32_t tokens;         /* rows of x (B * S for a padded batch), >= 0 */
+  int32_t hidden;         /* columns of x, multiple of 64 */
+  int32_t heads;          /* H >= 1 */
+  int32_t head_dim;       /* 128 */
+  int32_t section[3];     /* rotary pairs driven by t, h, w; sum == D/2 */
+  float theta;            /* rotary base, > 0 */
+  float eps;              /* RMSNorm epsilon, >= 0 */
+  float softmax_scale;    /* > 0, or <= 0 for 1/sqrt(D) */
+  int64_t x_stride;       /* elements between rows of x (multiple of 8) */
+  int64_t q_stride[2];    /* token, head strides of q_out (elements) */
+  int64_t k_stride[2];
+  int64_t v_stride[2];
+} mra_qkv_desc;
+
+size_t mrope_qkv_proj_workspace_size(const mra_qkv_desc* desc);
+
+int mrope_qkv_proj(const mra_qkv_desc* desc, const void* x, const uint8_t* w8, const float* w_scale,
+                   const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                   void* q_out, void* k_out, void* v_out, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* mrope_attn_status_string(int status);

@@ -32,7 +32,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(mrope_attn_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(mrope_\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
         "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
         "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
-        "mrope_attn_workspace_size"])
+        "mrope_attn_workspace_size", "mrope_qkv_proj", "mrope_qkv_proj_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -65,7 +65,7 @@ def test_desc_layout_matches_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 103
+    assert lib.mrope_attn_abi_version() == 104
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -328,3 +328,44 @@ def test_bwd_rejects_before_launch(lib, monkeypatch):
     monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
     assert _bwd(d, nbytes=need) == -8
     assert _bwd(d, nbytes=need, dg=None) == -8
+
+
+# ---------------------------------------------------------------- operands given / fp8 QKV
+def test_kprologue_none_needs_no_positions_or_table(lib):
+    d = desc(kprologue="none")
+    assert val(d, pos=None, gq=None, gk=None) == 0
+    assert val(desc(), pos=None) == -1                         # other modes still need them
+    dd = desc(batch=1, seq=4608, heads=32, text_pad=512, kprologue="none")
+    split = 128 * 2 * 256 * (128 // 2 + 2) * 4                 # the split records only
+    assert B.workspace_size(dd) == split
+    assert val(desc(kprologue=3, dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
+    # no backward on given operands
+    assert _bwd(desc(kprologue="none")) == -6
+
+
+def _qkv(d, **ptr):
+    p = dict(x=FAKE, w=FAKE, s=FAKE, pos=FAKE, gq=FAKE, gk=FAKE, q=FAKE, k=FAKE, v=FAKE, ws=FAKE,
+             n=1 << 40)
+    p.update(ptr)
+    return B.lib().mrope_qkv_proj(ctypes.byref(d), p["x"], p["w"], p["s"], p["pos"], p["gq"], p["gk"],
+                                  p["q"], p["k"], p["v"], p["ws"], p["n"], None)
+
+
+def test_qkv_proj_contract(lib, monkeypatch):
+    d = B.make_qkv_desc(4608, 4096, 32)
+    assert B.lib().mrope_qkv_proj_workspace_size(ctypes.byref(d)) == 4608 * 64 * 8
+    assert _qkv(B.make_qkv_desc(10, 100, 2)) == -2                       # hidden % 64
+    assert _qkv(B.make_qkv_desc(10, 128, 0)) == -2
+    assert _qkv(B.make_qkv_desc(10, 128, 2, head_dim=64, section=(8, 12, 12))) == -6
+    assert _qkv(B.make_qkv_desc(10, 128, 2, section=(16, 24, 23))) == -4
+    assert _qkv(B.make_qkv_desc(10, 128, 2, theta=0.0)) == -9
+    assert _qkv(B.make_qkv_desc(10, 128, 2, x_stride=100)) == -5
+    assert _qkv(B.make_qkv_desc(10, 128, 2, q_stride=(260, 128))) == -5
+    assert _qkv(B.make_qkv_desc(1 << 20, 1024, 2)) == -6               # 32-bit offsets into x
+    d = B.make_qkv_desc(10, 128, 2)
+    assert _qkv(d, w=None) == -1
+    assert _qkv(d, x=FAKE + 8) == -5
+    assert _qkv(d, n=10) == -7
+    assert _qkv(B.make_qkv_desc(0, 128, 2), x=None, ws=None, n=0) == 0
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _qkv(d) == -8
