@@ -167,6 +167,71 @@ def bench_cfg(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_qkv(args):
+    """The layer's attention input path at a configuration's shape: x [B*S,
+    hidden = H*D] bf16 through the fp8 e4m3 fused qkv weight with the
+    norm/rotation epilogue (one call), then the attention on those operands.
+    value = the projection's FLOP rate (2 * tokens * hidden * 3 H D)."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_qkv_proj
+    from diffusion_transformer_image_head_amd.workloads import CONFIGS, make_qkv_workload
+
+    lib()
+    c = CONFIGS[args.config]
+    h, d = c["heads"], c["head_dim"]
+    w = make_qkv_workload(c["batch"], h, d, c["section"], c["text_pad"], c["grid_h"], c["grid_w"],
+                          h * d, seed=c["seed"])
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    x = t(w.x).to(torch.bfloat16)
+    w8, wsc, pos, gq, gk = t(w.w8), t(w.w_scale), t(w.pos), t(w.gamma_q), t(w.gamma_k)
+    outs = tuple(torch.empty((w.x.shape[0], h, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+    b, s = w.batch, w.seq
+    q, k, v = (o.view(b, s, h, d) for o in outs)
+    att_out = torch.empty_like(q)
+    att_ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+
+    def proj():
+        mrope_qkv_proj(x, w8, wsc, pos, gq, gk, heads=h, section=w.section, out=outs, workspace=ws)
+
+    def attend():
+        mrope_attn(q, k, v, None, None, None, text_pad=w.text_pad, kprologue="none", out=att_out,
+                   workspace=att_ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_p = timed(proj)
+    ms_a = timed(attend)
+    value = w.flops() / (ms_p * 1e-3) / 1e12
+    att_flops = 4 * h * d * s * s * b
+    rec = {
+        "metric": "fp8 QKV projection + norm/rotation epilogue TFLOP/s (bf16 matrix cores)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_p, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x, N(0,1/hidden) weight quantized to e4m3 per row)",
+        "config": {"workload": f"{args.config} qkv: tokens={b * s} hidden={h * d} out={3 * h * d}"},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "rope_table_kernel + qkv_proj_kernel"},
+        "attention_on_operands": {"ms": round(ms_a, 5),
+                                  "TFLOP/s": round(att_flops / (ms_a * 1e-3) / 1e12, 3)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def bench_bwd(args):
     """Backward pass on a configuration: the forward runs once (untimed) for
     out and lse, then `steps` backward calls are timed. FLOPs: the usual 2.5x
@@ -231,6 +296,9 @@ def main():
                          "image-only unconditional pass in one grouped call")
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--qkv", action="store_true",
+                    help="time the fp8 QKV projection with the norm/rotation epilogue, then the "
+                         "attention on its operands (kprologue none)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv, dgammas) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -249,6 +317,9 @@ def main():
         return
     if args.backward:
         bench_bwd(args)
+        return
+    if args.qkv:
+        bench_qkv(args)
         return
 
     import numpy as np
