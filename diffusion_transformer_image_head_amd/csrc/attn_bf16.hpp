@@ -45,6 +45,9 @@
 namespace mra {
 
 constexpr float kRescaleLog2 = 8.0f;
+#ifndef MRA_FIXED_MAX
+#define MRA_FIXED_MAX 1
+#endif
 
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -430,6 +433,44 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   while (t < ntiles && skipped(t)) ++t;
   refresh_neg_m();
   bool first = true;
+#if MRA_FIXED_MAX
+  // QK-RMSNorm bounds every logit: |Q''.K'| <= |Q''| |K'| and |K'| <=
+  // max|gamma_k| sqrt(D) (a normalised row has mean square <= 1; the margin
+  // covers K''s bf16 rounding). When that bound m stays small enough that
+  // exp2(S - m) >= exp2(-2m) is a normal float, m serves as the row's
+  // "running max" from the start: no row max, no rescaling.
+  bool fixed_max = false;
+  if constexpr (!PRE) {
+    float gmax = fabsf(a.gk[lane]);
+    if constexpr (D > 64) gmax = fmaxf(gmax, fabsf(a.gk[lane + 64]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, o, 64));
+    const float kb = gmax * sqrtf((float)D) * (1.0f + 1.0f / 128);
+    bool big = false;
+    float mf[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) n2 += (float)qf[rb][c][e] * (float)qf[rb][c][e];
+      // padded query rows (whose output is zero whatever they hold) neither
+      // decide nor need the bound
+      mf[rb] = valid_row[rb] ? sqrtf(half_swap_sum(n2)) * kb : 0.f;
+      big = big || !(mf[rb] <= 60.f);
+    }
+    if (__builtin_amdgcn_ballot_w64(big) == 0) {
+      fixed_max = true;
+      first = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) mrun[rb] = mf[rb];
+      refresh_neg_m();
+    }
+  }
+#else
+  constexpr bool fixed_max = false;
+#endif
 
   // S^T = K'(t) Q'^T - m from K' buffer `kpar`: all K' fragments of the tile
   // are read first so the reads overlap each other and the MFMAs using them
@@ -478,6 +519,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
           for (int rb = 0; rb < RB; ++rb) st[rb][kb][i] = ok ? st[rb][kb][i] : -INFINITY;
         }
     }
+    if (!fixed_max) {
     // row max of this tile relative to the running max
     float mx[RB];
     bool grow = false;
@@ -510,6 +552,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
       }
       first = false;
       refresh_neg_m();
+    }
     }
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
