@@ -416,9 +416,16 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     lrun[rb] = 0.f;
     lrun2[rb] = 0.f;  // second partial row sum (two chains for latency)
   }
+  // -m broadcast over a lane's 16 accumulators: the C input of each tile's
+  // first Q.K' MFMA (read-only, so the tile loop copies nothing into S)
+  f32x16 negm_vec[RB];
   auto refresh_neg_m = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) neg_m[rb] = -mrun[rb];
+    for (int rb = 0; rb < RB; ++rb) {
+      neg_m[rb] = -mrun[rb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negm_vec[rb][i] = neg_m[rb];
+    }
   };
 
   // v-operand read roles (transposing LDS read): lane 16g + j of a 16-lane
@@ -484,18 +491,13 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
       for (int kb = 0; kb < NB; ++kb)
         kf[c][kb] = *(const bf16x8*)(src + k_lds_off<D>(kb * 32 + m, 2 * c + hf));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kb = 0; kb < NB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[rb][kb][i] = neg_m[rb];
-#pragma unroll
     for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c], st[rb][kb], 0, 0, 0);
+          st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c],
+                                                               c == 0 ? negm_vec[rb] : st[rb][kb], 0, 0, 0);
     // keep kAhead fragment reads in flight ahead of the MFMAs
     constexpr int kFrags = KC * NB, kAhead = kFrags / 2;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
