@@ -45,6 +45,12 @@
 namespace mra {
 
 constexpr float kRescaleLog2 = 8.0f;
+#ifndef MRA_KAHEAD
+#define MRA_KAHEAD 4
+#endif
+#ifndef MRA_PV_PACE
+#define MRA_PV_PACE 8
+#endif
 #ifndef MRA_FIXED_MAX
 #define MRA_FIXED_MAX 1
 #endif
@@ -499,7 +505,7 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
           st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c],
                                                                c == 0 ? negm_vec[rb] : st[rb][kb], 0, 0, 0);
     // keep kAhead fragment reads in flight ahead of the MFMAs
-    constexpr int kFrags = KC * NB, kAhead = kFrags / 2;
+    constexpr int kFrags = KC * NB, kAhead = MRA_KAHEAD > 0 ? MRA_KAHEAD : kFrags / 2;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
     for (int i = 0; i < kFrags; ++i) {
@@ -599,6 +605,17 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
           for (int rb = 0; rb < RB; ++rb)
             oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[rb][kb][u], oacc[rb][db], 0, 0, 0);
         }
+    if constexpr (MRA_PV_PACE > 0) {
+      // two transposing reads per MFMA; keep MRA_PV_PACE of them in flight
+      constexpr int vM = NB * 2 * DB, vA = MRA_PV_PACE;
+      __builtin_amdgcn_sched_group_barrier(0x100, vA, 0);
+#pragma unroll
+      for (int i = 0; i < vM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+        if (2 * i + 2 + vA <= 2 * vM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (2 * i + 1 + vA <= 2 * vM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
   };
 
   if (t < ntiles) {
