@@ -11,13 +11,14 @@
 //
 // One workgroup per (256 tokens, one head of Q, K or V = 128 output rows),
 // 4 waves of 64 tokens. Output transposed on the matrix cores:
-// C^T (rows x tokens) = W x^T with v_mfma_f32_32x32x16_bf16, A = W rows read
-// from LDS, B = the wave's x rows loaded straight into registers (each wave
-// owns its tokens). Each 64-wide hidden chunk of W arrives as fp8 by direct
-// loads into LDS (double-buffered), is widened once to bf16 in LDS by the
-// whole workgroup (v_cvt_scalef32_pk_bf16_fp8: exact for e4m3) and read by the
-// four waves; the row scale factors out of the sum and is applied in the
-// epilogue. A lane pair then holds all 128 rows of one token, so the RMSNorm
+// C^T (rows x tokens) = W x^T with v_mfma_f32_32x32x16_bf16, A = W rows and
+// B = x rows, both read from LDS. Each 32-wide hidden chunk of x (256 rows)
+// arrives by direct loads one chunk ahead (16 rows per load instruction,
+// instead of one row per lane); the W chunk arrives as fp8 two chunks ahead,
+// is widened once to bf16 in LDS by the whole workgroup one chunk ahead
+// (v_cvt_scalef32_pk_bf16_fp8: exact for e4m3; double-buffered, so one
+// barrier per chunk) and is read by the four waves; the row scale factors out
+// of the sum and is applied in the epilogue. A lane pair then holds all 128 rows of one token, so the RMSNorm
 // is lane-local plus one swap and each rotary pair (j, j + 64) sits in one
 // lane.
 #pragma once
@@ -42,70 +43,84 @@ struct QkvArgs {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(QkvArgs g) {
-  constexpr int KB = 64;              // hidden chunk
-  constexpr int W8B = D * KB;         // fp8 chunk bytes (8 KB)
+  constexpr int KB = 32;              // hidden chunk
+  constexpr int W8B = D * KB;         // fp8 chunk bytes (4 KB)
+  constexpr int XB = 256 * KB * 2;    // bf16 x chunk bytes (16 KB)
   constexpr int DB = D / 32, KS = KB / 16;
   static_assert(D == 128, "written for head_dim 128");
+  // x chunk: 256 token rows of 64 bytes; W chunk: 128 rows of 32 fp8 bytes,
+  // widened to 128 rows of 64 bytes. 16-byte chunk c of a 64-byte row r sits
+  // at c ^ ((r >> 2) & 3): 16 consecutive rows read at one chunk are
+  // conflict-free on 64 banks.
+  __shared__ __attribute__((aligned(1024))) char X0[XB];
+  __shared__ __attribute__((aligned(1024))) char X1[XB];
   __shared__ __attribute__((aligned(1024))) uint8_t W0[W8B];
   __shared__ __attribute__((aligned(1024))) uint8_t W1[W8B];
-  __shared__ __attribute__((aligned(1024))) char Wb[D * KB * 2];   // bf16, 128-byte rows
+  __shared__ __attribute__((aligned(1024))) char Wb0[D * KB * 2];
+  __shared__ __attribute__((aligned(1024))) char Wb1[D * KB * 2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 31, hf = lane >> 5;
+  // Logical tile order (each XCD runs a contiguous range): groups of GT
+  // token tiles; within a group, head after head, GT token tiles each. The
+  // workgroups resident together then share a few token tiles of x and a few
+  // heads of W per hidden chunk, so both are fetched into L2 a few times
+  // instead of x once per head.
+  constexpr int GT = 8;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = tile % g.n_mt, hb = tile / g.n_mt;     // hb in [0, 3H)
+  const int nh = 3 * g.H, full = g.n_mt / GT;
+  int mt, hb;
+  if (tile < full * GT * nh) {
+    const int tg = tile / (GT * nh), w = tile % (GT * nh);
+    hb = w / GT;
+    mt = tg * GT + w % GT;
+  } else {
+    const int r = tile - full * GT * nh, gsz = g.n_mt - full * GT;
+    hb = r / gsz;
+    mt = full * GT + r % gsz;
+  }
   const int part = hb / g.H, head = hb % g.H;
   const int t0 = mt * 256 + wave * 64;
+  auto swz = [](int r) { return (r >> 2) & 3; };
 
-  // x rows of this lane's two tokens: buffer loads, rows past M read zeros
+  // x chunk: run j of this wave = bytes [(wave*4+j)*1024, +1024) = rows
+  // (wave*4+j)*16 + L/4, physical chunk L%4; rows past M read zeros
   const uint32_t xnrec = (uint32_t)((int64_t)g.M * g.xs * 2);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(g.x, xnrec);
-  uint32_t xoff[2];
+  uint32_t xoff[4];
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int tok = t0 + tb * 32 + m;
-    xoff[tb] = tok < g.M ? (uint32_t)(((int64_t)tok * g.xs + hf * 8) * 2) : xnrec;
+  for (int j = 0; j < 4; ++j) {
+    const int r = (wave * 4 + j) * 16 + (lane >> 2);
+    const int tok = mt * 256 + r;
+    const int c = (lane & 3) ^ swz(r);
+    xoff[j] = tok < g.M ? (uint32_t)(((int64_t)tok * g.xs + c * 8) * 2) : xnrec;
   }
-  auto load_x = [&](int kc, u32x4 (&xf)[2][KS]) {
+  auto issue_x = [&](int kc, char* dst) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        xf[tb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-            xrs, xoff[tb] == xnrec ? xnrec : xoff[tb] + (uint32_t)((kc * KB + ks * 16) * 2), 0, 0);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr_t)(dst + (wave * 4 + j) * 1024), 16,
+                                               xoff[j] == xnrec ? xnrec : xoff[j] + kc * KB * 2, 0, 0, 0);
   };
-  // W chunk: run j of this wave = bytes [(wave*2+j)*1024, +1024) = rows
-  // (wave*2+j)*16 + L/4, bytes (L%4)*16 of the row
+  // W chunk: wave's run = bytes [wave*1024, +1024) = rows wave*32 + L/2, bytes (L%2)*16
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(g.w8 + (int64_t)hb * D * g.hidden, (uint32_t)(D * g.hidden));
-  uint32_t woff[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (wave * 2 + j) * 16 + (lane >> 2);
-    woff[j] = (uint32_t)(row * g.hidden + (lane & 3) * 16);
-  }
+  const uint32_t woff = (uint32_t)((wave * 32 + (lane >> 1)) * g.hidden + (lane & 1) * 16);
   auto issue_w = [&](int kc, uint8_t* dst) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(dst + (wave * 2 + j) * 1024), 16,
-                                               woff[j] + kc * KB, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(dst + wave * 1024), 16, woff + kc * KB, 0, 0, 0);
   };
-  // widen the fp8 chunk to bf16: thread t converts row t/2, bytes (t%2)*32..+31
-  // into logical chunks (t%2)*4 .. +3 of the bf16 row (chunk c at c ^ swz(row))
-  auto widen = [&](const uint8_t* src) {
+  // widen: thread t converts row t/2, fp8 bytes (t%2)*16..+15 into logical
+  // chunks (t%2)*2, +1 of the bf16 row
+  auto widen = [&](const uint8_t* src, char* Wb) {
     const int row = tid >> 1, h = tid & 1;
-    const u32x4 a = *(const u32x4*)(src + row * KB + h * 32);
-    const u32x4 b = *(const u32x4*)(src + row * KB + h * 32 + 16);
-    const uint32_t wv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    const int swz = (row >> 1) & 7;
+    const u32x4 a = *(const u32x4*)(src + row * KB + h * 16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < 2; ++c) {
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const uint32_t w = wv[2 * c + e];
+        const uint32_t w = a[2 * c + e];
         o[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
         o[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
       }
-      *(u32x4*)(Wb + row * (KB * 2) + (((h * 4 + c) ^ swz) << 4)) = o;
+      *(u32x4*)(Wb + row * (KB * 2) + (((h * 2 + c) ^ swz(row)) << 4)) = o;
     }
   };
 
@@ -117,35 +132,43 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(QkvArgs g) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tb][db][i] = 0.f;
 
+  // Chunk i: W8(i) lands two steps ahead and is widened one step ahead, x(i)
+  // lands one step ahead; one barrier per step: after it x(i) and W8(i+1)
+  // have landed, Wb(i) is complete, and every wave is done with x(i-1),
+  // Wb(i-1) and W8(i).
   const int nk = g.hidden / KB;
-  u32x4 xf[2][KS], xn[2][KS];
+  issue_x(0, X0);
   issue_w(0, W0);
-  load_x(0, xn);
+  if (nk > 1) issue_w(1, W1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  widen(W0, Wb0);
   auto step = [&](int kc, auto parity) {
     constexpr int cur = decltype(parity)::value;
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // W8(kc) landed; every wave is done with Wb
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) xf[tb][ks] = xn[tb][ks];
-    if (kc + 1 < nk) {
-      issue_w(kc + 1, cur ? W0 : W1);
-      load_x(kc + 1, xn);
-    }
-    widen(cur ? W1 : W0);
     __syncthreads();
+    if (kc + 1 < nk) issue_x(kc + 1, cur ? X0 : X1);
+    if (kc + 2 < nk) issue_w(kc + 2, cur ? W1 : W0);
+    if (kc + 1 < nk) widen(cur ? W0 : W1, cur ? Wb0 : Wb1);
+    const char* Wb = cur ? Wb1 : Wb0;
+    const char* Xs = cur ? X1 : X0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 xb[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int r = wave * 64 + tb * 32 + m;
+        xb[tb] = *(const bf16x8*)(Xs + r * (KB * 2) + (((2 * ks + hf) ^ swz(r)) << 4));
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int row = db * 32 + m;
-        const bf16x8 a = *(const bf16x8*)(Wb + row * (KB * 2) + (((2 * ks + hf) ^ ((row >> 1) & 7)) << 4));
+        const bf16x8 a = *(const bf16x8*)(Wb + row * (KB * 2) + (((2 * ks + hf) ^ swz(row)) << 4));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
-          acc[tb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, xf[tb][ks]),
-                                                                acc[tb][db], 0, 0, 0);
+          acc[tb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[tb], acc[tb][db], 0, 0, 0);
       }
+    }
   };
   for (int kc = 0; kc < nk; kc += 2) {
     step(kc, Parity<0>{});
