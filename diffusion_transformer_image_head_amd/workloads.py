@@ -14,7 +14,8 @@ token (r, c) gets (L, L + r, L + c) with L the item's true text length; a
 padded text slot keeps (i, i, i) (it is masked anyway).
 
 Values: q, k, v ~ N(0, sigma^2) drawn in float32, gamma_q, gamma_k ~
-U[0.5, 1.5), in that order from ``numpy.random.default_rng(seed)``. For bf16
+U[0.5, 1.5) ([D] each, or [H, D] each with ``gamma_per_head``), in that
+order from ``numpy.random.default_rng(seed)``. For bf16
 workloads q, k, v are rounded to bf16 (round-to-nearest-even) and returned as
 float32 arrays holding bf16-exact values, so the device cast is exact.
 """
@@ -45,6 +46,11 @@ CONFIGS = {
                 text_lens=None, grid_h=64, grid_w=64, sigma=1.0, dtype="bf16", seed=5),
     "2048px": dict(batch=1, heads=32, head_dim=128, section=(16, 24, 24), text_pad=512,
                    text_lens=None, grid_h=128, grid_w=128, sigma=1.0, dtype="bf16", seed=6),
+    # the 1024px ragged batch under the other conventions: a gamma per head
+    # and interleaved rotary pairs (2j, 2j + 1)
+    "conv": dict(batch=2, heads=32, head_dim=128, section=(16, 24, 24), text_pad=512,
+                 text_lens=(77, 512), grid_h=64, grid_w=64, sigma=1.0, dtype="bf16", seed=7,
+                 gamma_per_head=True, rope_pairs="interleaved"),
 }
 
 
@@ -54,7 +60,7 @@ class Workload:
     k: np.ndarray
     v: np.ndarray
     pos: np.ndarray        # [B, S, 3] int32, (t, h, w)
-    gamma_q: np.ndarray    # [D] float32
+    gamma_q: np.ndarray    # [D] or [H, D] float32
     gamma_k: np.ndarray
     seq_lens: np.ndarray | None   # [B] int32 or None (no padding)
     text_pad: int
@@ -63,6 +69,7 @@ class Workload:
     theta: float = 10000.0
     eps: float = 1e-6
     grid: tuple = field(default=(0, 0))
+    rope_pairs: str = "half"   # rotary pair layout: "half" or "interleaved"
 
     @property
     def shape(self):
@@ -110,7 +117,8 @@ def positions(batch: int, text_pad: int, grid_h: int, grid_w: int, text_lens=Non
 
 def make_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w,
                   text_lens=None, sigma=1.0, dtype="bf16", seed=0,
-                  theta=10000.0, eps=1e-6) -> Workload:
+                  theta=10000.0, eps=1e-6, gamma_per_head=False,
+                  rope_pairs="half") -> Workload:
     """Draw one seeded workload (see the module docstring for the recipe)."""
     s = text_pad + grid_h * grid_w
     rng = np.random.default_rng(seed)
@@ -122,8 +130,9 @@ def make_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w,
         q *= np.float32(sigma)
         k *= np.float32(sigma)
         v *= np.float32(sigma)
-    gq = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
-    gk = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    gshape = (heads, head_dim) if gamma_per_head else head_dim
+    gq = rng.uniform(0.5, 1.5, gshape).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, gshape).astype(np.float32)
     if dtype == "bf16":
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     elif dtype != "fp32":
@@ -132,7 +141,7 @@ def make_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w,
     return Workload(q=q, k=k, v=v, pos=positions(batch, text_pad, grid_h, grid_w, text_lens),
                     gamma_q=gq, gamma_k=gk, seq_lens=lens, text_pad=text_pad,
                     section=tuple(section), dtype=dtype, theta=theta, eps=eps,
-                    grid=(grid_h, grid_w))
+                    grid=(grid_h, grid_w), rope_pairs=rope_pairs)
 
 
 def config_workload(name: str) -> Workload:
@@ -155,6 +164,7 @@ class VarlenWorkload:
     dtype: str
     theta: float = 10000.0
     eps: float = 1e-6
+    rope_pairs: str = "half"
 
     @property
     def max_seqlen(self):
@@ -166,18 +176,19 @@ class VarlenWorkload:
 
 
 def make_varlen_workload(heads, head_dim, section, text_lens, grids, sigma=1.0, dtype="bf16",
-                         seed=0) -> VarlenWorkload:
+                         seed=0, gamma_per_head=False, rope_pairs="half") -> VarlenWorkload:
     """Sequence b = text_lens[b] real text tokens then a grids[b] = (gh, gw)
     image raster, each drawn as its own unpadded one-item workload (seed +
     b), with the first item's gammas shared by all."""
     parts = [make_workload(1, heads, head_dim, section, int(l), gh, gw, sigma=sigma, dtype=dtype,
-                           seed=seed + b) for b, (l, (gh, gw)) in enumerate(zip(text_lens, grids))]
+                           seed=seed + b, gamma_per_head=gamma_per_head)
+             for b, (l, (gh, gw)) in enumerate(zip(text_lens, grids))]
     lens = [p.q.shape[1] for p in parts]
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     cat = lambda f: np.ascontiguousarray(np.concatenate([getattr(p, f)[0] for p in parts]))  # noqa: E731
     return VarlenWorkload(q=cat("q"), k=cat("k"), v=cat("v"), pos=cat("pos"),
                           gamma_q=parts[0].gamma_q, gamma_k=parts[0].gamma_k, cu_seqlens=cu,
-                          section=tuple(section), dtype=dtype)
+                          section=tuple(section), dtype=dtype, rope_pairs=rope_pairs)
 
 
 @dataclass
@@ -197,13 +208,14 @@ class QkvWorkload:
     head_dim: int
     text_pad: int
     section: tuple
+    rope_pairs: str = "half"
 
     def flops(self):
         return 2 * self.x.shape[0] * self.x.shape[1] * self.w8.shape[0]
 
 
 def make_qkv_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w, hidden,
-                      seed=0) -> QkvWorkload:
+                      seed=0, gamma_per_head=False, rope_pairs="half") -> QkvWorkload:
     """x ~ N(0, 1) rounded to bf16; a dense weight ~ N(0, 1/hidden) quantized
     per output row to float8 e4m3 (scale = row max / 448, round to nearest via
     the library's float8_e4m3fn cast), as the checkpoint stores it."""
@@ -216,9 +228,10 @@ def make_qkv_workload(batch, heads, head_dim, section, text_pad, grid_h, grid_w,
     w = rng.standard_normal((n, hidden), dtype=np.float32) / np.float32(np.sqrt(hidden))
     scale = (np.abs(w).max(axis=1) / 448.0).astype(np.float32)
     codes = torch.from_numpy(w / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    gq = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
-    gk = rng.uniform(0.5, 1.5, head_dim).astype(np.float32)
+    gshape = (heads, head_dim) if gamma_per_head else head_dim
+    gq = rng.uniform(0.5, 1.5, gshape).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, gshape).astype(np.float32)
     pos = positions(batch, text_pad, grid_h, grid_w).reshape(m, 3)
     return QkvWorkload(x=x, w8=np.ascontiguousarray(codes), w_scale=scale, pos=np.ascontiguousarray(pos),
                        gamma_q=gq, gamma_k=gk, batch=batch, seq=s, heads=heads, head_dim=head_dim,
-                       text_pad=text_pad, section=tuple(section))
+                       text_pad=text_pad, section=tuple(section), rope_pairs=rope_pairs)

@@ -19,15 +19,16 @@ by the chain rule, step by step in reverse order of the forward:
      dgamma_d = sum_rows dx_hat_d x_d r,
      dx_d = r gamma_d dx_hat_d - (r^3 / D) x_d sum_e dx_hat_e gamma_e x_e.
 Padded query rows have a constant zero output, padded keys are excluded:
-neither carries gradient. gamma_q and gamma_k are shared by every head and
-token, so their gradients sum over all valid rows.
+neither carries gradient. A [D] gamma is shared by every head and token, so
+its gradient sums over all valid rows; an [H, D] gamma gets one gradient row
+per head, summed over that head's rows.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from oracle.reference import axis_of_pair, inv_freq, valid_tokens
+from oracle.reference import axis_of_pair, inv_freq, pair_slots, valid_tokens
 
 
 def _angles(pos, section, head_dim, theta):
@@ -37,18 +38,23 @@ def _angles(pos, section, head_dim, theta):
     return np.cos(ang)[:, :, None, :], np.sin(ang)[:, :, None, :]
 
 
-def _rotate(x, c, s, sign):
-    """Turn every pair (x_j, x_{j+D/2}) by sign * phi."""
-    half = x.shape[-1] // 2
-    x1, x2 = x[..., :half], x[..., half:]
-    return np.concatenate([x1 * c - sign * x2 * s, x2 * c + sign * x1 * s], axis=-1)
+def _rotate(x, c, s, sign, pairs):
+    """Turn every rotary pair (x_a, x_b) of the given layout by sign * phi."""
+    ia, ib = pair_slots(x.shape[-1], pairs)
+    x1, x2 = x[..., ia], x[..., ib]
+    out = np.empty_like(x)
+    out[..., ia] = x1 * c - sign * x2 * s
+    out[..., ib] = x2 * c + sign * x1 * s
+    return out
 
 
 def oracle_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, dout, *, text_pad: int,
-               section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None):
+               section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
+               rope_pairs: str = "half"):
     """Gradients of sum(dout * out) for out = oracle_fwd(...).
 
-    Returns (dq, dk, dv [B, S, H, D], dgamma_q, dgamma_k [D]) in float64.
+    Returns (dq, dk, dv [B, S, H, D], dgamma_q, dgamma_k) in float64; each
+    dgamma has its gamma's shape ([D] or [H, D]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -67,8 +73,8 @@ def oracle_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, dout, *, text_pad: int,
 
     xq, rq = norm(q, gq)
     xk, rk = norm(k, gk)
-    qr = _rotate(xq, c, s, +1.0)
-    kr = _rotate(xk, c, s, +1.0)
+    qr = _rotate(xq, c, s, +1.0, rope_pairs)
+    kr = _rotate(xk, c, s, +1.0, rope_pairs)
     valid = valid_tokens(b_, s_, text_pad, seq_lens)
 
     dqr = np.zeros_like(q)
@@ -92,11 +98,11 @@ def oracle_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, dout, *, text_pad: int,
             dqr[b, :, h, :] = scale * ds @ kr[b, kv, h, :]
             dkr[b, kv, h, :] = scale * ds.T @ qr[b, :, h, :]
 
-    dxq = _rotate(dqr, c, s, -1.0)
-    dxk = _rotate(dkr, c, s, -1.0)
+    dxq = _rotate(dqr, c, s, -1.0, rope_pairs)
+    dxk = _rotate(dkr, c, s, -1.0, rope_pairs)
 
     def norm_bwd(x, r, g, dxh):
-        dg = np.sum(dxh * x * r, axis=(0, 1, 2))
+        dg = np.sum(dxh * x * r, axis=(0, 1) if g.ndim == 2 else (0, 1, 2))
         inner = np.sum(dxh * g * x, axis=-1, keepdims=True)
         dx = r * g * dxh - (r ** 3 / x.shape[-1]) * x * inner
         return dx, dg

@@ -25,8 +25,10 @@ def _axis(j: int, section) -> int:
     return 2
 
 
-def _prologue_row(x, gamma, p3, section, theta, eps):
-    """RMSNorm then M-RoPE of one head row x (a list of D floats)."""
+def _prologue_row(x, gamma, p3, section, theta, eps, pairs="half"):
+    """RMSNorm then M-RoPE of one head row x (a list of D floats). Rotary
+    pair j is the complex number (x_j, x_{j+D/2}) for pairs="half", or
+    (x_2j, x_2j+1) for pairs="interleaved"."""
     d = len(x)
     half = d // 2
     acc = 0.0
@@ -37,15 +39,17 @@ def _prologue_row(x, gamma, p3, section, theta, eps):
     out = [0.0] * d
     for j in range(half):
         phi = float(p3[_axis(j, section)]) * (float(theta) ** (-(2.0 * j) / d))
-        z = complex(xn[j], xn[j + half]) * cmath.exp(1j * phi)
-        out[j] = z.real
-        out[j + half] = z.imag
+        a, b = (j, j + half) if pairs == "half" else (2 * j, 2 * j + 1)
+        z = complex(xn[a], xn[b]) * cmath.exp(1j * phi)
+        out[a] = z.real
+        out[b] = z.imag
     return out
 
 
 def brute_fwd(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad,
-              section, theta=10000.0, eps=1e-6, scale=None):
-    """Returns (out, lse) as nested lists: out[b][s][h][d], lse[b][h][s]."""
+              section, theta=10000.0, eps=1e-6, scale=None, rope_pairs="half"):
+    """Returns (out, lse) as nested lists: out[b][s][h][d], lse[b][h][s].
+    gamma_q and gamma_k are one list of D weights, or one such list per head."""
     bn = len(q)
     sn = len(q[0])
     hn = len(q[0][0])
@@ -61,9 +65,11 @@ def brute_fwd(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad,
             lb = min(max(int(seq_lens[b]), 0), text_pad)
             real = [(s >= text_pad) or (s < lb) for s in range(sn)]
         for h in range(hn):
-            qp = [_prologue_row(q[b][s][h], gamma_q, pos[b][s], section, theta, eps)
+            gq = gamma_q[h] if hasattr(gamma_q[0], "__len__") else gamma_q
+            gk = gamma_k[h] if hasattr(gamma_k[0], "__len__") else gamma_k
+            qp = [_prologue_row(q[b][s][h], gq, pos[b][s], section, theta, eps, rope_pairs)
                   for s in range(sn)]
-            kp = [_prologue_row(k[b][s][h], gamma_k, pos[b][s], section, theta, eps)
+            kp = [_prologue_row(k[b][s][h], gk, pos[b][s], section, theta, eps, rope_pairs)
                   for s in range(sn)]
             for i in range(sn):
                 if not real[i]:

@@ -40,8 +40,9 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def oracle_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, head_dim: int,
                     section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
-                    qscale: float = 1.0, rows=None):
-    """x [M, hidden], w8 [3 H D, hidden] e4m3 codes, w_scale [3 H D], pos [M, 3].
+                    qscale: float = 1.0, rows=None, rope_pairs: str = "half"):
+    """x [M, hidden], w8 [3 H D, hidden] e4m3 codes, w_scale [3 H D], pos [M, 3],
+    gamma_q and gamma_k [D] or [H, D].
     Returns (q_op, k_op, v_op), each [R, H, D] float64 for the rows `rows`
     (all by default)."""
     x = np.asarray(x, dtype=np.float64)
@@ -53,6 +54,6 @@ def oracle_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, head_d
     k = y[:, hd:2 * hd].reshape(len(rows), heads, head_dim)
     v = y[:, 2 * hd:].reshape(len(rows), heads, head_dim)
     p = np.asarray(pos)[rows][None]                            # [1, R, 3]
-    q_op = qscale * mrope(rms_norm(q[None], gamma_q, eps), p, section, theta)[0]
-    k_op = mrope(rms_norm(k[None], gamma_k, eps), p, section, theta)[0]
+    q_op = qscale * mrope(rms_norm(q[None], gamma_q, eps), p, section, theta, rope_pairs)[0]
+    k_op = mrope(rms_norm(k[None], gamma_k, eps), p, section, theta, rope_pairs)[0]
     return q_op, k_op, v

@@ -27,9 +27,10 @@ taken exactly as stored (bf16 and fp32 widen to fp64 exactly).
 
 Readings of points the pages leave open (each is a descriptor field or an
 input, so both sides use the same value): epsilon inside the root, weight
-applied as x_hat * gamma, norm before rotation, half-split rotary pairs
-(j, j + D/2), one global frequency ladder theta^(-2j/D) across the three
-axes, contiguous sections in t, h, w order, softmax scale D^-1/2, no causal
+applied as x_hat * gamma (gamma shared by the heads by default, or one per
+head), norm before rotation, half-split rotary pairs (j, j + D/2) by default
+(interleaved pairs (2j, 2j + 1) on request), one global frequency ladder
+theta^(-2j/D) across the three axes, contiguous sections in t, h, w order, softmax scale D^-1/2, no causal
 mask, equal head counts for Q, K and V.
 """
 
@@ -73,18 +74,37 @@ def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     """Per-row RMSNorm over the last axis: x * (mean(x^2) + eps)^-1/2 * gamma.
 
     The QK-RMSNorm of the Ideogram 4.0 announcement thread, applied per head
-    (the last axis is head_dim).
+    (the last axis is head_dim). gamma is [D] (one weight shared by every
+    head) or, for x [..., H, D], [H, D] (a weight per head); either
+    broadcasts against x.
     """
     x = np.asarray(x, dtype=np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + np.float64(eps)) * np.asarray(gamma, dtype=np.float64)
 
 
-def mrope(x: np.ndarray, pos: np.ndarray, section, theta: float) -> np.ndarray:
+def pair_slots(head_dim: int, pairs: str = "half"):
+    """Element indices (first, second) of every rotary pair j < D/2.
+
+    "half": pair j is (j, j + D/2), the rotate-half layout; "interleaved":
+    pair j is (2j, 2j + 1). The pages name neither; both are conventions in
+    use for rotary encodings, and a descriptor field picks one.
+    """
+    half = head_dim // 2
+    j = np.arange(half)
+    if pairs == "half":
+        return j, j + half
+    if pairs == "interleaved":
+        return 2 * j, 2 * j + 1
+    raise ValueError(f"unknown rotary pair layout {pairs!r}")
+
+
+def mrope(x: np.ndarray, pos: np.ndarray, section, theta: float, pairs: str = "half") -> np.ndarray:
     """3D multimodal RoPE on x [B, S, H, D] with positions pos [B, S, 3].
 
-    Pair j = (x_j, x_{j+D/2}) is turned by the angle pos[axis(j)] * inv_freq(j):
-    x'_j = x_j cos - x_{j+D/2} sin,  x'_{j+D/2} = x_{j+D/2} cos + x_j sin.
+    Pair j = (x_a, x_b) (slots from :func:`pair_slots`) is turned by the
+    angle pos[axis(j)] * inv_freq(j):
+    x'_a = x_a cos - x_b sin,  x'_b = x_b cos + x_a sin.
     (Ideogram 4.0 announcement thread: 3D multimodal RoPE; "Ideogram 4 deep
     dive", section 6 part 3: rotary encoding extended to three axes.)
     """
@@ -96,9 +116,13 @@ def mrope(x: np.ndarray, pos: np.ndarray, section, theta: float) -> np.ndarray:
     ang = p[:, :, axis] * inv_freq(d, theta)           # [B, S, half]
     c = np.cos(ang)[:, :, None, :]                     # broadcast over heads
     s = np.sin(ang)[:, :, None, :]
-    x1 = x[..., :half]
-    x2 = x[..., half:]
-    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+    ia, ib = pair_slots(d, pairs)
+    x1 = x[..., ia]
+    x2 = x[..., ib]
+    out = np.empty_like(x)
+    out[..., ia] = x1 * c - x2 * s
+    out[..., ib] = x2 * c + x1 * s
+    return out
 
 
 def valid_tokens(batch: int, seq: int, text_pad: int, seq_lens=None) -> np.ndarray:
@@ -153,11 +177,12 @@ def attention(qr: np.ndarray, kr: np.ndarray, v: np.ndarray, valid: np.ndarray,
 
 def oracle_fwd(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
                section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
-               scale=None, rows=None, heads=None):
+               scale=None, rows=None, heads=None, rope_pairs: str = "half"):
     """The whole hot path: RMSNorm -> M-RoPE on Q and K, then attention.
 
     q, k, v: [B, S, H, D] (any real dtype; widened to float64).
-    pos: [B, S, 3] integer (t, h, w) positions.  gamma_q, gamma_k: [D].
+    pos: [B, S, 3] integer (t, h, w) positions.  gamma_q, gamma_k: [D] or
+    [H, D].  rope_pairs: "half" or "interleaved" (:func:`pair_slots`).
     seq_lens: [B] true text lengths (<= text_pad) or None for no padding.
     scale: softmax scale; None or <= 0 means head_dim ** -0.5.
     Returns (out [B, R, Hs, D], lse [B, Hs, R]) in float64.
@@ -167,14 +192,15 @@ def oracle_fwd(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     b_, s_, h_, d_ = q.shape
     if scale is None or scale <= 0:
         scale = 1.0 / np.sqrt(np.float64(d_))
-    qr = mrope(rms_norm(q, gamma_q, eps), pos, section, theta)
-    kr = mrope(rms_norm(k, gamma_k, eps), pos, section, theta)
+    qr = mrope(rms_norm(q, gamma_q, eps), pos, section, theta, rope_pairs)
+    kr = mrope(rms_norm(k, gamma_k, eps), pos, section, theta, rope_pairs)
     valid = valid_tokens(b_, s_, text_pad, seq_lens)
     return attention(qr, kr, v, valid, scale, rows=rows, heads=heads)
 
 
 def oracle_fwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, *, section=(16, 24, 24),
-                      theta: float = 10000.0, eps: float = 1e-6, scale=None):
+                      theta: float = 10000.0, eps: float = 1e-6, scale=None,
+                      rope_pairs: str = "half"):
     """Packed variable-length form of the same path: sequence b is tokens
     [cu_seqlens[b], cu_seqlens[b+1]) of q, k, v [T, H, D] and pos [T, 3] (its
     true-length text tokens, then its image tokens), and attends to its own
@@ -196,7 +222,8 @@ def oracle_fwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, *, section=(16
             continue
         o, l = oracle_fwd(q[None, a0:a1], np.asarray(k)[None, a0:a1], np.asarray(v)[None, a0:a1],
                           np.asarray(pos)[None, a0:a1], gamma_q, gamma_k, None, text_pad=0,
-                          section=section, theta=theta, eps=eps, scale=scale)
+                          section=section, theta=theta, eps=eps, scale=scale,
+                          rope_pairs=rope_pairs)
         out[a0:a1] = o[0]
         lse[:, a0:a1] = l[0]
     return out, lse

@@ -436,4 +436,105 @@ def pin_varlen_sequences_are_isolated():
     assert np.max(np.abs(out[~keep] - out2[~keep])) > 1e-3
 
 
+# --------------------------------------------------------------------- conventions
+def pin_interleaved_text_tokens_are_complex_rope():
+    """Interleaved pairs (2j, 2j + 1) on a text token (t = h = w = m): each
+    pair, read as the complex number x_2j + i x_2j+1, is multiplied by
+    exp(i m theta^(-2j/D)) -- the complex form of 1D RoPE, evaluated with
+    numpy's complex type -- and equals RoFormer's rotation matrix directly."""
+    rng = np.random.default_rng(42)
+    for d, sec in ((64, (8, 12, 12)), (128, (16, 24, 24)), (128, (24, 20, 20))):
+        for m in (0, 1, 5, 77, 511):
+            x = rng.standard_normal(d)
+            y = ref.mrope(x[None, None, None, :], np.array([[[m, m, m]]]), sec, 1e4,
+                          "interleaved")[0, 0, 0]
+            z = x.view(np.complex128) * np.exp(1j * m * 1e4 ** (-np.arange(d // 2) * 2.0 / d))
+            assert np.max(np.abs(y - z.view(np.float64))) < 1e-12, (d, sec, m)
+            assert np.max(np.abs(y - _rope_1d_roformer(x, float(m), 1e4))) < 1e-12
+
+
+def pin_interleaved_brute():
+    """Scalar loops (complex form, per-row Python) == vectorised oracle with
+    interleaved pairs, on a ragged batch with distinct t, h, w positions."""
+    w = make_workload(2, 2, 16, (2, 3, 3), 5, 3, 4, text_lens=(2, 5), seed=43, dtype="fp32",
+                      rope_pairs="interleaved")
+    out, lse = _run(w, rope_pairs="interleaved")
+    bo, bl = brute_fwd(w.q.tolist(), w.k.tolist(), w.v.tolist(), w.pos.tolist(),
+                       w.gamma_q.tolist(), w.gamma_k.tolist(), w.seq_lens.tolist(),
+                       text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
+                       rope_pairs="interleaved")
+    assert np.max(np.abs(out - np.array(bo))) < 1e-12
+    fin = np.isfinite(lse)
+    assert np.max(np.abs(lse[fin] - np.array(bl)[fin])) < 1e-12
+    # and the layout matters: the half-split result differs
+    o2, _ = _run(w)
+    assert np.max(np.abs(o2 - out)) > 1e-3
+
+
+def pin_interleaved_is_half_split_of_permuted_dims():
+    """Dot products ignore the order of head_dim, and RMSNorm only scales it,
+    so interleaved pairs on (q, k, gamma) equal half-split pairs on the same
+    tensors with their dims reordered (even dims, then odd dims); v and the
+    output are untouched."""
+    w = make_workload(2, 3, 32, (4, 6, 6), 6, 3, 4, text_lens=(1, 6), seed=44, dtype="fp32")
+    out, lse = _run(w, rope_pairs="interleaved")
+    p = np.concatenate([np.arange(0, 32, 2), np.arange(1, 32, 2)])
+    o2, l2 = ref.oracle_fwd(w.q[..., p], w.k[..., p], w.v, w.pos, w.gamma_q[p], w.gamma_k[p],
+                            w.seq_lens, text_pad=w.text_pad, section=w.section, theta=w.theta,
+                            eps=w.eps)
+    assert np.max(np.abs(out - o2)) < 1e-12
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(l2)) and np.max(np.abs(lse[fin] - l2[fin])) < 1e-12
+
+
+def pin_interleaved_relative_positions():
+    """Relative encoding holds for interleaved pairs too: shifting both
+    tokens' positions per axis leaves q.k, and a change of one axis's
+    difference changes it."""
+    rng = np.random.default_rng(45)
+    d, sec = 128, (16, 24, 24)
+    q = rng.standard_normal((1, 1, 1, d))
+    k = rng.standard_normal((1, 1, 1, d))
+    dot = lambda pq, pk: float((ref.mrope(q, pq[None, None], sec, 1e4, "interleaved")  # noqa: E731
+                                * ref.mrope(k, pk[None, None], sec, 1e4, "interleaved")).sum())
+    for _ in range(10):
+        pq = rng.integers(0, 600, size=3)
+        pk = rng.integers(0, 600, size=3)
+        sh = rng.integers(-300, 300, size=3)
+        a = dot(pq, pk)
+        assert abs(a - dot(pq + sh, pk + sh)) < 1e-10 * (1 + abs(a))
+        for ax in range(3):
+            pk2 = pk.copy()
+            pk2[ax] += 7
+            assert abs(dot(pq, pk2) - a) > 1e-6
+
+
+def pin_per_head_gamma():
+    """An [H, D] gamma: head h of the output equals a one-head run on head h
+    alone with gamma[h] as its [D] weight; equal rows reproduce the shared
+    [D] gamma; the scalar loops agree."""
+    w = make_workload(2, 3, 16, (2, 3, 3), 4, 2, 3, text_lens=(1, 4), seed=46, dtype="fp32",
+                      gamma_per_head=True)
+    assert w.gamma_q.shape == (3, 16)
+    for pairs in ("half", "interleaved"):
+        out, lse = _run(w, rope_pairs=pairs)
+        for h in range(3):
+            oh, lh = ref.oracle_fwd(w.q[:, :, h:h + 1], w.k[:, :, h:h + 1], w.v[:, :, h:h + 1],
+                                    w.pos, w.gamma_q[h], w.gamma_k[h], w.seq_lens,
+                                    text_pad=w.text_pad, section=w.section, rope_pairs=pairs)
+            assert np.max(np.abs(out[:, :, h:h + 1] - oh)) < 1e-13
+            fin = np.isfinite(lh)
+            assert np.max(np.abs(lse[:, h:h + 1][fin] - lh[fin])) < 1e-13
+        bo, _ = brute_fwd(w.q.tolist(), w.k.tolist(), w.v.tolist(), w.pos.tolist(),
+                          w.gamma_q.tolist(), w.gamma_k.tolist(), w.seq_lens.tolist(),
+                          text_pad=w.text_pad, section=w.section, rope_pairs=pairs)
+        assert np.max(np.abs(out - np.array(bo))) < 1e-12
+    shared = make_workload(2, 3, 16, (2, 3, 3), 4, 2, 3, text_lens=(1, 4), seed=46, dtype="fp32")
+    o1, _ = _run(shared)
+    shared.gamma_q = np.tile(shared.gamma_q, (3, 1))
+    shared.gamma_k = np.tile(shared.gamma_k, (3, 1))
+    o2, _ = _run(shared)
+    assert np.array_equal(o1, o2)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,7 +38,7 @@ def _m_eps_outside(x, gamma, eps):
 
 
 
-def _flip(x, pos, section, theta):
+def _flip(x, pos, section, theta, pairs="half"):
     # rotation with the sine terms' signs swapped (x'_j = x_j c + x_{j+h} s, ...)
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
@@ -46,10 +46,11 @@ def _flip(x, pos, section, theta):
     ang = np.asarray(pos, dtype=np.float64)[:, :, ref.axis_of_pair(section, h)] * ref.inv_freq(d, theta)
     c = np.cos(ang)[:, :, None, :]
     s = np.sin(ang)[:, :, None, :]
-    return np.concatenate([x[..., :h] * c + x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], -1)
+    y = np.concatenate([x[..., :h] * c + x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], -1)
+    return y if pairs == "half" else _orig["mrope"](x, pos, section, theta, pairs)
 
 
-def _m_interleaved(x, pos, section, theta):
+def _m_interleaved(x, pos, section, theta, pairs="half"):
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
     h = d // 2
@@ -58,6 +59,26 @@ def _m_interleaved(x, pos, section, theta):
     perm[1::2] = np.arange(h) + h
     inv = np.argsort(perm)
     return _orig["mrope"](x[..., inv], pos, section, theta)[..., perm]
+
+
+def _m_pairs_ignored(x, pos, section, theta, pairs="half"):
+    # the layout argument dropped: interleaved requests get half-split pairs
+    return _orig["mrope"](x, pos, section, theta)
+
+
+def _m_interleaved_swapped(x, pos, section, theta, pairs="half"):
+    # interleaved pairs read as (2j + 1, 2j): the rotation runs backwards
+    if pairs != "interleaved":
+        return _orig["mrope"](x, pos, section, theta, pairs)
+    x = np.asarray(x, dtype=np.float64)
+    sw = np.arange(x.shape[-1]) ^ 1
+    return _orig["mrope"](x[..., sw], pos, section, theta, pairs)[..., sw]
+
+
+def _m_gamma_head0(x, gamma, eps):
+    # a per-head gamma collapsed to its first row
+    g = np.asarray(gamma, dtype=np.float64)
+    return _orig["rms_norm"](x, g[0] if g.ndim == 2 else g, eps)
 
 
 def _m_axis_order(section, half):
@@ -106,7 +127,8 @@ def _m_no_mask(batch, seq, text_pad, seq_lens=None):
 
 MUTANTS = [
     ("rms_norm", _m_no_gamma), ("rms_norm", _m_sum_not_mean), ("rms_norm", _m_eps_outside),
-    ("mrope", _flip), ("mrope", _m_interleaved),
+    ("mrope", _flip), ("mrope", _m_interleaved), ("mrope", _m_pairs_ignored),
+    ("mrope", _m_interleaved_swapped), ("rms_norm", _m_gamma_head0),
     ("axis_of_pair", _m_axis_order), ("axis_of_pair", _m_axis_all_t),
     ("inv_freq", _m_freq),
     ("attention", _m_no_scale), ("attention", _m_transposed), ("attention", _m_no_zero_rows),

@@ -21,19 +21,24 @@ def _case(seed=70, **kw):
 
 def _grads(w, do):
     return bwd.oracle_bwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens, do,
-                          text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps)
+                          text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
+                          rope_pairs=w.rope_pairs)
 
 
 def pin_bwd_finite_differences():
     """Directional derivatives of sum(dO * O) by central differences of the
-    forward oracle, for every input that has a gradient."""
-    for w in (_case(), _case(seed=71, text_lens=None, section=(4, 2, 2), text_pad=3)):
+    forward oracle, for every input that has a gradient; also under the other
+    conventions (a gamma per head, interleaved rotary pairs)."""
+    for w in (_case(), _case(seed=71, text_lens=None, section=(4, 2, 2), text_pad=3),
+              _case(seed=75, gamma_per_head=True, rope_pairs="interleaved"),
+              _case(seed=76, rope_pairs="interleaved", text_lens=None, text_pad=2)):
         rng = np.random.default_rng(5)
         do = rng.standard_normal(w.q.shape)
 
         def loss(q, k, v, gq, gk):
             o, _ = oracle_fwd(q, k, v, w.pos, gq, gk, w.seq_lens, text_pad=w.text_pad,
-                              section=w.section, theta=w.theta, eps=w.eps)
+                              section=w.section, theta=w.theta, eps=w.eps,
+                              rope_pairs=w.rope_pairs)
             return float(np.sum(o * do))
 
         args = [np.asarray(a, dtype=np.float64) for a in (w.q, w.k, w.v, w.gamma_q, w.gamma_k)]
@@ -80,8 +85,26 @@ def pin_bwd_position_shift_invariance():
         assert np.max(np.abs(a - b)) < 1e-10
 
 
+def pin_bwd_shared_gamma_is_sum_over_heads():
+    """A [D] gamma is every head's weight at once, so its gradient is the sum
+    over heads of the gradient of an [H, D] gamma with equal rows."""
+    w = _case(seed=77)
+    do = np.random.default_rng(9).standard_normal(w.q.shape)
+    g_shared = _grads(w, do)
+    h = w.q.shape[2]
+    w.gamma_q = np.tile(w.gamma_q, (h, 1))
+    w.gamma_k = np.tile(w.gamma_k, (h, 1))
+    g_head = _grads(w, do)
+    assert g_head[3].shape == (h, w.q.shape[3])
+    for i in range(3):
+        assert np.max(np.abs(g_shared[i] - g_head[i])) < 1e-13
+    for i in (3, 4):
+        assert np.max(np.abs(g_shared[i] - g_head[i].sum(axis=0))) < 1e-12
+        assert np.max(np.abs(g_head[i][0] - g_head[i][1])) > 1e-6
+
+
 PINS = [pin_bwd_finite_differences, pin_bwd_padded_tokens_have_no_gradient, pin_bwd_dv_column_sum,
-        pin_bwd_position_shift_invariance]
+        pin_bwd_position_shift_invariance, pin_bwd_shared_gamma_is_sum_over_heads]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -89,16 +112,20 @@ def test_bwd_pin(pin):
     pin()
 
 
-def _m_rotate_forward_only(x, c, s, sign):
+def _m_rotate_forward_only(x, c, s, sign, pairs="half"):
     half = x.shape[-1] // 2
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)   # ignores sign
 
 
-def _m_rotate_swapped_halves(x, c, s, sign):
+def _m_rotate_swapped_halves(x, c, s, sign, pairs="half"):
     half = x.shape[-1] // 2
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x2 * c - sign * x1 * s, x1 * c + sign * x2 * s], axis=-1)
+
+
+def _m_rotate_pairs_ignored(x, c, s, sign, pairs="half"):
+    return _real_rotate(x, c, s, sign, "half")
 
 
 def _m_angles_no_freq(pos, section, head_dim, theta):
@@ -112,7 +139,10 @@ def _m_valid_all(batch, seq, text_pad, seq_lens=None):
     return np.ones((batch, seq), dtype=bool)
 
 
+_real_rotate = bwd._rotate
+
 MUTANTS = [("_rotate", _m_rotate_forward_only), ("_rotate", _m_rotate_swapped_halves),
+           ("_rotate", _m_rotate_pairs_ignored),
            ("_angles", _m_angles_no_freq), ("valid_tokens", _m_valid_all)]
 
 

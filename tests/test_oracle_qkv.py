@@ -3,6 +3,7 @@ library's float8_e4m3fn, the projection against scalar loops, and the
 composition with the attention oracle."""
 
 import numpy as np
+import pytest
 
 import oracle.qkv as qkv
 from oracle.reference import mrope, oracle_fwd, rms_norm
@@ -52,11 +53,17 @@ def test_projection_against_scalar_loops():
     assert np.max(np.abs(k - mrope(rms_norm(kr, gk, 1e-6), pos[None], (2, 1, 1), 1e4)[0])) < 1e-12
 
 
-def test_rows_subset_and_composition_with_attention():
+@pytest.mark.parametrize("per_head,pairs", [(False, "half"), (True, "interleaved")])
+def test_rows_subset_and_composition_with_attention(per_head, pairs):
     x, w8, sc, pos, gq, gk = _case(seed=1, m=9, hidden=32, heads=2, d=16)
-    full = qkv.oracle_qkv_proj(x, w8, sc, pos, gq, gk, heads=2, head_dim=16, section=(2, 3, 3))
+    if per_head:
+        rng = np.random.default_rng(3)
+        gq = rng.uniform(0.5, 1.5, (2, 16))
+        gk = rng.uniform(0.5, 1.5, (2, 16))
+    full = qkv.oracle_qkv_proj(x, w8, sc, pos, gq, gk, heads=2, head_dim=16, section=(2, 3, 3),
+                               rope_pairs=pairs)
     sub = qkv.oracle_qkv_proj(x, w8, sc, pos, gq, gk, heads=2, head_dim=16, section=(2, 3, 3),
-                              rows=[2, 5])
+                              rows=[2, 5], rope_pairs=pairs)
     for a, b in zip(full, sub):
         assert np.max(np.abs(a[[2, 5]] - b)) < 1e-12
     # q_op / k_op are exactly the attention oracle's rotated operands: attention
@@ -64,7 +71,8 @@ def test_rows_subset_and_composition_with_attention():
     w = qkv.e4m3_decode(w8) * sc[:, None]
     y = x @ w.T
     q, k, v = (y[:, i * 32:(i + 1) * 32].reshape(1, 9, 2, 16) for i in range(3))
-    out, _ = oracle_fwd(q, k, v, pos[None], gq, gk, None, text_pad=0, section=(2, 3, 3))
+    out, _ = oracle_fwd(q, k, v, pos[None], gq, gk, None, text_pad=0, section=(2, 3, 3),
+                        rope_pairs=pairs)
     qo, ko, vo = full
     z = np.einsum("qhd,khd->hqk", qo, ko) / 4.0
     p = np.exp(z - z.max(-1, keepdims=True))
