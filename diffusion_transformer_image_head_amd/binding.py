@@ -18,6 +18,16 @@ LIB_PATH = os.path.join(HERE, "libmrope_attn.so")
 MRA_BF16, MRA_FP32 = 0, 1
 KPRO_AUTO, KPRO_FUSED, KPRO_PREPASS = 0, 1, 2
 _KPRO = {"auto": KPRO_AUTO, "fused": KPRO_FUSED, "prepass": KPRO_PREPASS}
+ROPE_HALF, ROPE_INTERLEAVED = 0, 1
+_PAIRS = {"half": ROPE_HALF, "interleaved": ROPE_INTERLEAVED}
+
+
+def _pairs(rope_pairs) -> int:
+    if isinstance(rope_pairs, str):
+        if rope_pairs not in _PAIRS:
+            raise ValueError(f"rope_pairs must be one of {sorted(_PAIRS)}")
+        return _PAIRS[rope_pairs]
+    return int(rope_pairs)
 
 
 class Desc(ctypes.Structure):
@@ -30,6 +40,7 @@ class Desc(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("kprologue", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("rope_pairs", ctypes.c_int32), ("gamma_per_head", ctypes.c_int32),
     ]
 
 
@@ -50,6 +61,7 @@ class QkvDesc(ctypes.Structure):
         ("theta", ctypes.c_float), ("eps", ctypes.c_float), ("softmax_scale", ctypes.c_float),
         ("x_stride", ctypes.c_int64), ("q_stride", ctypes.c_int64 * 2),
         ("k_stride", ctypes.c_int64 * 2), ("v_stride", ctypes.c_int64 * 2),
+        ("rope_pairs", ctypes.c_int32), ("gamma_per_head", ctypes.c_int32),
     ]
 
 
@@ -121,9 +133,12 @@ def status_string(status: int) -> str:
 
 def make_desc(batch, seq, heads, head_dim, *, text_pad, section=(16, 24, 24), theta=10000.0,
               eps=1e-6, scale=None, dtype=MRA_BF16, kprologue="auto",
-              q_stride=None, k_stride=None, v_stride=None, o_stride=None) -> Desc:
+              q_stride=None, k_stride=None, v_stride=None, o_stride=None,
+              rope_pairs="half", gamma_per_head=False) -> Desc:
     """Build a descriptor; strides default to contiguous [B, S, H, D]."""
     d = Desc()
+    d.rope_pairs = _pairs(rope_pairs)
+    d.gamma_per_head = int(gamma_per_head)
     d.batch, d.seq, d.heads, d.head_dim, d.text_pad = batch, seq, heads, head_dim, text_pad
     d.section[:] = [int(x) for x in section]
     d.theta, d.eps = float(theta), float(eps)
@@ -153,7 +168,7 @@ def _bsd_strides(t):
 
 
 def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_pad, section,
-             theta, eps, scale, kprologue):
+             theta, eps, scale, kprologue, rope_pairs="half"):
     """Shape/dtype/device checks; returns (desc, out, lse, seq_lens)."""
     import torch
 
@@ -178,9 +193,12 @@ def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_
     if pos is not None and (pos.dtype != torch.int32 or tuple(pos.shape) != (b, s, 3)
                             or not pos.is_contiguous()):
         raise ValueError("pos must be contiguous int32 [B, S, 3]")
+    # gammas: both [D] (shared by the heads) or both [H, D] (one per head)
+    gshape = None if gamma_q is None else tuple(gamma_q.shape)
     for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
-        if g is not None and (g.dtype != torch.float32 or tuple(g.shape) != (d,) or not g.is_contiguous()):
-            raise ValueError(f"{name} must be contiguous float32 [D]")
+        if g is not None and (g.dtype != torch.float32 or tuple(g.shape) not in ((d,), (h, d))
+                              or tuple(g.shape) != gshape or not g.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [D] or [H, D], like the other gamma")
     if seq_lens is not None:
         if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (b,) or not seq_lens.is_cuda:
             raise ValueError("seq_lens must be a GPU int32 [B] tensor")
@@ -190,27 +208,30 @@ def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_
     lse = torch.empty((b, h, s), dtype=torch.float32, device=q.device) if return_lse else None
     desc = make_desc(b, s, h, d, text_pad=text_pad, section=section, theta=theta, eps=eps,
                      scale=scale, dtype=dt, kprologue=kprologue, q_stride=_bsd_strides(q),
-                     k_stride=_bsd_strides(k), v_stride=_bsd_strides(v), o_stride=_bsd_strides(out))
+                     k_stride=_bsd_strides(k), v_stride=_bsd_strides(v), o_stride=_bsd_strides(out),
+                     rope_pairs=rope_pairs, gamma_per_head=gshape is not None and len(gshape) == 2)
     return desc, out, lse, seq_lens
 
 
 def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
                section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
                return_lse: bool = False, kprologue="auto", out=None, workspace=None,
-               stage: str = "fwd"):
+               stage: str = "fwd", rope_pairs="half"):
     """Fused QK-RMSNorm + 3D M-RoPE joint attention on the current HIP stream.
 
     q, k, v: [B, S, H, D] bf16 or fp32 GPU tensors (head_dim contiguous; any
     batch/token/head strides, e.g. views of one fused qkv buffer).
-    pos: [B, S, 3] int32 (t, h, w). gamma_q, gamma_k: [D] fp32.
+    pos: [B, S, 3] int32 (t, h, w). gamma_q, gamma_k: [D] fp32 (shared by
+    the heads) or [H, D] (one per head).
     seq_lens: [B] int32 true text lengths (<= text_pad) or None.
+    rope_pairs: "half" (pairs (j, j + D/2)) or "interleaved" ((2j, 2j + 1)).
     Returns out [B, S, H, D] (q's dtype), and lse [B, H, S] fp32 if asked.
     """
     import torch
 
     desc, out, lse, seq_lens = _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse,
                                         text_pad=text_pad, section=section, theta=theta, eps=eps,
-                                        scale=scale, kprologue=kprologue)
+                                        scale=scale, kprologue=kprologue, rope_pairs=rope_pairs)
     need = workspace_size(desc)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -267,7 +288,7 @@ def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", wo
     conditional [text + image] and unconditional [image only] passes of one
     guided sampling step). ``problems`` is a list of dicts with the arguments
     of :func:`mrope_attn`: q, k, v, pos, gamma_q, gamma_k, and optionally
-    seq_lens, text_pad (default 0), section, theta, eps, scale, out.
+    seq_lens, text_pad (default 0), section, theta, eps, scale, rope_pairs, out.
     Returns the list of outputs (of (out, lse) pairs if ``return_lse``)."""
     import torch
 
@@ -279,7 +300,8 @@ def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", wo
             p["q"], p["k"], p["v"], p["pos"], p["gamma_q"], p["gamma_k"], p.get("seq_lens"),
             p.get("out"), return_lse, text_pad=p.get("text_pad", 0),
             section=p.get("section", (16, 24, 24)), theta=p.get("theta", 10000.0),
-            eps=p.get("eps", 1e-6), scale=p.get("scale"), kprologue=kprologue)
+            eps=p.get("eps", 1e-6), scale=p.get("scale"), kprologue=kprologue,
+            rope_pairs=p.get("rope_pairs", "half"))
         descs.append(desc)
         probs.append(Problem(p["q"].data_ptr(), p["k"].data_ptr(), p["v"].data_ptr(),
                              p["pos"].data_ptr(), p["gamma_q"].data_ptr(), p["gamma_k"].data_ptr(),
@@ -304,7 +326,7 @@ def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", wo
 def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: int, *,
                       section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
                       scale=None, return_lse: bool = False, kprologue="auto", out=None,
-                      workspace=None):
+                      workspace=None, rope_pairs="half"):
     """Packed variable-length form: q, k, v [T, H, D], pos [T, 3] int32,
     cu_seqlens [B + 1] int32 on the GPU (sequence b = tokens cu[b]:cu[b+1]),
     max_seqlen >= every sequence length. Returns out [T, H, D] (and lse
@@ -324,7 +346,7 @@ def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: in
         out = torch.empty((t, h, d), dtype=q.dtype, device=q.device)
     desc, out4, lse, _ = _checked(q[None], k[None], v[None], pos[None], gamma_q, gamma_k, None,
                                   out[None], False, text_pad=0, section=section, theta=theta,
-                                  eps=eps, scale=scale, kprologue=kprologue)
+                                  eps=eps, scale=scale, kprologue=kprologue, rope_pairs=rope_pairs)
     lse = torch.empty((h, t), dtype=torch.float32, device=q.device) if return_lse else None
     desc.batch = nseq
     need = int(lib().mrope_attn_varlen_workspace_size(ctypes.byref(desc), int(max_seqlen)))
@@ -343,15 +365,16 @@ def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: in
 
 def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, text_pad: int,
                    section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6, scale=None,
-                   dq=None, dk=None, dv=None, workspace=None):
+                   dq=None, dk=None, dv=None, workspace=None, rope_pairs="half"):
     """Backward of :func:`mrope_attn` (bf16, head_dim 128): gradients of
     sum(dout * out) given the forward's out and lse. Returns (dq, dk, dv,
-    dgamma_q, dgamma_k); dq/dk/dv take q/k/v's strides, dout out's."""
+    dgamma_q, dgamma_k); dq/dk/dv take q/k/v's strides, dout out's, and each
+    dgamma its gamma's shape."""
     import torch
 
     desc, out_, _, seq_lens = _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, False,
                                        text_pad=text_pad, section=section, theta=theta, eps=eps,
-                                       scale=scale, kprologue="auto")
+                                       scale=scale, kprologue="auto", rope_pairs=rope_pairs)
     if tuple(dout.shape) != tuple(q.shape) or _bsd_strides(dout) != _bsd_strides(out):
         raise ValueError("dout must have out's shape and strides")
     b, s, h, d = q.shape
@@ -363,8 +386,8 @@ def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, 
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         if t.shape != ref.shape or _bsd_strides(t) != _bsd_strides(ref):
             raise ValueError(f"{name} must have the strides of its input")
-    dgq = torch.empty(d, dtype=torch.float32, device=q.device)
-    dgk = torch.empty(d, dtype=torch.float32, device=q.device)
+    dgq = torch.empty(gamma_q.shape, dtype=torch.float32, device=q.device)
+    dgk = torch.empty(gamma_k.shape, dtype=torch.float32, device=q.device)
     need = int(lib().mrope_attn_bwd_workspace_size(ctypes.byref(desc)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -382,8 +405,10 @@ def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, 
 
 def make_qkv_desc(tokens, hidden, heads, head_dim=128, *, section=(16, 24, 24), theta=10000.0,
                   eps=1e-6, scale=None, x_stride=None, q_stride=None, k_stride=None,
-                  v_stride=None) -> QkvDesc:
+                  v_stride=None, rope_pairs="half", gamma_per_head=False) -> QkvDesc:
     d = QkvDesc()
+    d.rope_pairs = _pairs(rope_pairs)
+    d.gamma_per_head = int(gamma_per_head)
     d.tokens, d.hidden, d.heads, d.head_dim = tokens, hidden, heads, head_dim
     d.section[:] = [int(x) for x in section]
     d.theta, d.eps = float(theta), float(eps)
@@ -396,12 +421,14 @@ def make_qkv_desc(tokens, hidden, heads, head_dim=128, *, section=(16, 24, 24), 
 
 
 def mrope_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, section=(16, 24, 24),
-                   theta: float = 10000.0, eps: float = 1e-6, scale=None, out=None, workspace=None):
+                   theta: float = 10000.0, eps: float = 1e-6, scale=None, out=None, workspace=None,
+                   rope_pairs="half"):
     """fp8 e4m3 QKV projection with the norm/rotation epilogue.
 
     x [M, hidden] bf16, w8 [3 H D, hidden] uint8 (e4m3 codes), w_scale [3 H D]
-    fp32, pos [M, 3] int32, gammas [D] fp32. Returns (q_op, k_op, v), each
-    [M, H, D] bf16: the operands mrope_attn takes with kprologue="none"."""
+    fp32, pos [M, 3] int32, gammas [D] or [H, D] fp32. Returns (q_op, k_op,
+    v), each [M, H, D] bf16: the operands mrope_attn takes with
+    kprologue="none"."""
     import torch
 
     for name, t in (("x", x), ("w8", w8), ("w_scale", w_scale), ("pos", pos), ("gamma_q", gamma_q),
@@ -411,7 +438,11 @@ def mrope_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, section
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be bf16 [M, hidden] with contiguous rows")
     m, hidden = x.shape
-    d = gamma_q.numel()
+    d = gamma_q.shape[-1]
+    for name, g in (("gamma_q", gamma_q), ("gamma_k", gamma_k)):
+        if (g.dtype != torch.float32 or tuple(g.shape) not in ((d,), (heads, d))
+                or g.shape != gamma_q.shape or not g.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous float32 [D] or [H, D], like the other gamma")
     if w8.dtype != torch.uint8 or tuple(w8.shape) != (3 * heads * d, hidden) or not w8.is_contiguous():
         raise ValueError("w8 must be contiguous uint8 [3 H D, hidden]")
     if w_scale.dtype != torch.float32 or w_scale.numel() != 3 * heads * d or not w_scale.is_contiguous():
@@ -422,7 +453,8 @@ def mrope_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, section
         out = tuple(torch.empty((m, heads, d), dtype=torch.bfloat16, device=x.device) for _ in range(3))
     st = [(t.stride(0), t.stride(1)) for t in out]
     desc = make_qkv_desc(m, hidden, heads, d, section=section, theta=theta, eps=eps, scale=scale,
-                         x_stride=x.stride(0), q_stride=st[0], k_stride=st[1], v_stride=st[2])
+                         x_stride=x.stride(0), q_stride=st[0], k_stride=st[1], v_stride=st[2],
+                         rope_pairs=rope_pairs, gamma_per_head=gamma_q.dim() == 2)
     need = int(lib().mrope_qkv_proj_workspace_size(ctypes.byref(desc)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)

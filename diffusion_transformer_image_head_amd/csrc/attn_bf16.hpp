@@ -242,12 +242,35 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
     const float c2 = a.c2;
     // (cos, sin) of this token's pairs from the table the prologue pass wrote
     const float2* csrow = a.cs + ((int64_t)bl * Sx + tok0 + min(row[rb], S - 1)) * (D / 2);
+    const float* gq = a.gq + head * a.gqs;
+    if (a.inter) {
+      // pairs (2j, 2j + 1): elements e, e + 1 of one chunk, pair index
+      // (c*16 + hf*8 + e) / 2; Q' keeps the element order of q
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const f32x4 ga = *(const f32x4*)(gq + c * 16 + hf * 8);
+        const f32x4 gb = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
+        const f32x4 t01 = *(const f32x4*)(csrow + c * 8 + hf * 4);
+        const f32x4 t23 = *(const f32x4*)(csrow + c * 8 + hf * 4 + 2);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float g1 = e < 4 ? ga[e] : gb[e - 4];
+          const float g2 = e < 4 ? ga[e + 1] : gb[e - 3];
+          const f32x4 t = e < 4 ? t01 : t23;
+          const float cs = t[(e & 2)], sn = t[(e & 2) + 1];
+          const float u = x[c][e] * r * g1;
+          const float w = x[c][e + 1] * r * g2;
+          qf[rb][c][e] = (__bf16)((u * cs - w * sn) * c2);
+          qf[rb][c][e + 1] = (__bf16)((w * cs + u * sn) * c2);
+        }
+      }
+    } else
 #pragma unroll
     for (int c = 0; c < KC / 2; ++c) {
-      const f32x4 g1a = *(const f32x4*)(a.gq + c * 16 + hf * 8);
-      const f32x4 g1b = *(const f32x4*)(a.gq + c * 16 + hf * 8 + 4);
-      const f32x4 g2a = *(const f32x4*)(a.gq + D / 2 + c * 16 + hf * 8);
-      const f32x4 g2b = *(const f32x4*)(a.gq + D / 2 + c * 16 + hf * 8 + 4);
+      const f32x4 g1a = *(const f32x4*)(gq + c * 16 + hf * 8);
+      const f32x4 g1b = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
+      const f32x4 g2a = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8);
+      const f32x4 g2b = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8 + 4);
       f32x4 t4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) t4[e] = *(const f32x4*)(csrow + c * 16 + hf * 8 + 2 * e);
@@ -336,9 +359,10 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
         const int n = n0 + fk_key[i];
         const uint32_t off = key_ok(n) ? (uint32_t)((n * krow + fk_c[i] * 8) * 2) : knrec;
         fkr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-        const int j0 = (fk_c[i] % (CPR / 2)) * 8 + (fk_c[i] >= CPR / 2 ? 4 : 0);
+        // half-split pairs: lanes c and c^1 share one group of 8 pair
+        // angles and each fetches 4; interleaved: chunk c holds pairs 4c..4c+3
+        const int j0 = a.inter ? 4 * fk_c[i] : (fk_c[i] % (CPR / 2)) * 8 + (fk_c[i] >= CPR / 2 ? 4 : 0);
         const float2* cp = a.cs + ((int64_t)bl * Sx + tok0 + min(n, S - 1)) * (D / 2) + j0;
-        // lanes c and c^1 share one group of 8 pair angles: each fetches 4
 #pragma unroll
         for (int e = 0; e < 4; ++e) fcs[i][e] = cp[e];
       }
@@ -363,29 +387,39 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
         const float r = rsqrtf(ss * (1.0f / D) + a.eps);
         const int c = fk_c[i];
         const bool first = c < CPR / 2;
+        const float* gk = a.gk + head * a.gqs;
         float y[8], px[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * a.gk[c * 8 + e];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) px[e] = __shfl_xor(y[e], 1, 64);
-        float2 cs8[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 mine = fcs[i][e];
-          const float2 other = make_float2(__shfl_xor(mine.x, 1, 64), __shfl_xor(mine.y, 1, 64));
-          cs8[e] = first ? mine : other;
-          cs8[4 + e] = first ? other : mine;
-        }
+        for (int e = 0; e < 8; ++e) y[e] = x[e] * r * gk[c * 8 + e];
         u32x4 o;
+        if (a.inter) {
+          // pairs (2j, 2j + 1) lie inside the chunk: elements e, e + 1
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float z[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int q = 2 * e + h;
-            z[h] = first ? (y[q] * cs8[q].x - px[q] * cs8[q].y) : (y[q] * cs8[q].x + px[q] * cs8[q].y);
+          for (int e = 0; e < 8; e += 2) {
+            const float2 t = fcs[i][e >> 1];
+            o[e >> 1] = pack_bf16(y[e] * t.x - y[e + 1] * t.y, y[e + 1] * t.x + y[e] * t.y);
           }
-          o[e] = pack_bf16(z[0], z[1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) px[e] = __shfl_xor(y[e], 1, 64);
+          float2 cs8[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 mine = fcs[i][e];
+            const float2 other = make_float2(__shfl_xor(mine.x, 1, 64), __shfl_xor(mine.y, 1, 64));
+            cs8[e] = first ? mine : other;
+            cs8[4 + e] = first ? other : mine;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float z[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int q = 2 * e + h;
+              z[h] = first ? (y[q] * cs8[q].x - px[q] * cs8[q].y) : (y[q] * cs8[q].x + px[q] * cs8[q].y);
+            }
+            o[e] = pack_bf16(z[0], z[1]);
+          }
         }
         // LDS row holding key fk_key: inverse of key_of_row within its 32-block
         const int kk = fk_key[i], w5 = kk & 31;
@@ -454,8 +488,9 @@ __global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(
   // "running max" from the start: no row max, no rescaling.
   bool fixed_max = false;
   if constexpr (!PRE) {
-    float gmax = fabsf(a.gk[lane]);
-    if constexpr (D > 64) gmax = fmaxf(gmax, fabsf(a.gk[lane + 64]));
+    const float* gk = a.gk + head * a.gqs;
+    float gmax = fabsf(gk[lane]);
+    if constexpr (D > 64) gmax = fmaxf(gmax, fabsf(gk[lane + 64]));
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, o, 64));
     const float kb = gmax * sqrtf((float)D) * (1.0f + 1.0f / 128);

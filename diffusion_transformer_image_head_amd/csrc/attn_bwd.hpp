@@ -90,18 +90,35 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs g) {
 // Transpose rotation and RMSNorm backward of one row whose gradient w.r.t.
 // the rotated, normalised row is held transposed across a lane pair: lane
 // (m, hf) holds dims db*32 + (r/4)*8 + hf*4 + r%4 (r < 16, db < D/32) in
-// acc[db][r], scaled by `mult`; rotary partners j and j + D/2 sit in the same
-// lane (db and db + D/64). Writes the bf16 input gradient of the row to dst
-// (if in_seq; zeros for an invalid row) and returns this lane's gamma
-// gradient contributions in dg (zero for an invalid row).
+// acc[db][r], scaled by `mult`. Rotary partners sit in the same lane: j and
+// j + D/2 in db and db + D/64, or (inter) 2j and 2j + 1 in r and r + 1.
+// Writes the bf16 input gradient of the row to dst (if in_seq; zeros for an
+// invalid row) and returns this lane's gamma gradient contributions in dg
+// (zero for an invalid row).
 template <int D>
 __device__ __forceinline__ void rope_rms_bwd(const f32x16 (&acc)[D / 32], float mult,
                                              const uint16_t* xrow, const float* gamma,
                                              const float2* csrow, float eps, bool valid,
-                                             bool in_seq, uint16_t* dst, int hf,
+                                             bool in_seq, uint16_t* dst, int hf, bool inter,
                                              float (&dg)[D / 32][16]) {
   constexpr int DB = D / 32, HB = DB / 2;
   float dx[DB][16], x[DB][16];
+  if (inter) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        // dims d0 .. d0 + 3 are pairs d0/2 and d0/2 + 1
+        const f32x4 c01 = *(const f32x4*)(csrow + (db * 32 + gq * 8 + hf * 4) / 2);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float cs = c01[e], sn = c01[e + 1];
+          const float d1 = acc[db][gq * 4 + e] * mult, d2 = acc[db][gq * 4 + e + 1] * mult;
+          dx[db][gq * 4 + e] = d1 * cs + d2 * sn;
+          dx[db][gq * 4 + e + 1] = d2 * cs - d1 * sn;
+        }
+      }
+  } else
 #pragma unroll
   for (int db = 0; db < HB; ++db)
 #pragma unroll
@@ -438,9 +455,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     const uint16_t* xrow = (const uint16_t*)a.k + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
     const float2* csrow = a.cs + ((int64_t)b * S + kc) * (D / 2);
     uint16_t* dst = (uint16_t*)g.dk + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
-    rope_rms_bwd<D>(dkacc, kLn2, xrow, a.gk, csrow, a.eps, kvalid, kin, dst, hf, dg);
+    rope_rms_bwd<D>(dkacc, kLn2, xrow, a.gk + head * a.gqs, csrow, a.eps, kvalid, kin, dst, hf,
+                    a.inter, dg);
   }
-  dgamma_partial<D>(dg, red, g.dgk_part + (int64_t)blockIdx.x * D, wave, lane);
+  dgamma_partial<D>(dg, red, g.dgk_part + (int64_t)tile * D, wave, lane);
 }
 
 // dQ: one workgroup per (batch, head, 128 queries), 32 per wave; key tiles of
@@ -594,30 +612,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
     const uint16_t* xrow = (const uint16_t*)a.q + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
     const float2* csrow = a.cs + ((int64_t)b * S + qc) * (D / 2);
     uint16_t* dst = (uint16_t*)g.dq + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
-    rope_rms_bwd<D>(dqacc, a.scale, xrow, a.gq, csrow, a.eps, qvalid, qin, dst, hf, dg);
+    rope_rms_bwd<D>(dqacc, a.scale, xrow, a.gq + head * a.gqs, csrow, a.eps, qvalid, qin, dst, hf,
+                    a.inter, dg);
   }
-  dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)blockIdx.x * D, wave, lane);
+  dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)tile * D, wave, lane);
 }
 
-// gamma gradient = sum of the workgroup partials in a fixed order: thread
-// (grp, d) of 8 x D sums partials grp, grp + 8, ... with four interleaved
-// accumulators, then the 8 x 4 sums are added in a fixed order. blockIdx.y
-// picks the gradient (0: gamma_q, 1: gamma_k).
+// gamma gradient = sum of the workgroup partials in a fixed order. The
+// partials of tile (b, h, t) sit at row (b * H + h) * n_t + t. Workgroup
+// (which, h) -- which 0: gamma_q, 1: gamma_k -- sums the n partials of its
+// gradient row h: partial i < n is row (i / run) * stride + h * run + i % run
+// (a shared [D] gamma: one row, run = n = every tile, stride 0; an [H, D]
+// gamma: row h, run = n_t, stride = H * n_t, n = B * n_t). Thread (grp, d)
+// of 8 x D sums partials grp, grp + 8, ... with four interleaved
+// accumulators, then the 8 x 4 sums are added in a fixed order.
 template <int D>
 __global__ __launch_bounds__(8 * D) void bwd_dgamma_kernel(const float* part_q, const float* part_k, int n,
-                                                          float* out_q, float* out_k) {
+                                                          int run, int64_t stride, float* out_q,
+                                                          float* out_k) {
   __shared__ float red[8][D];
-  const float* part = blockIdx.x ? part_k : part_q;
-  float* out = blockIdx.x ? out_k : out_q;
+  const int which = blockIdx.x & 1, h = blockIdx.x >> 1;
+  const float* part = (which ? part_k : part_q) + (int64_t)h * run * D;
+  float* out = which ? out_k : out_q;
   if (!out) return;
+  out += (int64_t)h * D;
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
+  auto at = [&](int i) { return part[((int64_t)(i / run) * stride + i % run) * D + d]; };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int i = grp;
   for (; i + 24 < n; i += 32) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += part[(int64_t)(i + 8 * u) * D + d];
+    for (int u = 0; u < 4; ++u) acc[u] += at(i + 8 * u);
   }
-  for (int u = 0; i < n; i += 8, ++u) acc[u & 3] += part[(int64_t)i * D + d];
+  for (int u = 0; i < n; i += 8, ++u) acc[u & 3] += at(i);
   red[grp][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (grp == 0) {

@@ -15,20 +15,22 @@
 namespace mra {
 
 // RMSNorm then M-RoPE of one fp32 row x[D] in place, for a token at (pt, ph, pw).
+// Rotary pair j is elements (j, j + D/2), or (2j, 2j + 1) when inter is set.
 template <int D>
 __device__ __forceinline__ void prologue_row_f32(float* x, const float* g, const Rope& rope,
-                                                 int pt, int ph, int pw, float eps) {
+                                                 int pt, int ph, int pw, float eps, bool inter) {
   constexpr int HALF = D / 2;
   float ss = 0.f;
   for (int d = 0; d < D; ++d) ss += x[d] * x[d];
   const float r = 1.0f / sqrtf(ss / D + eps);
   for (int j = 0; j < HALF; ++j) {
-    const float u = x[j] * r * g[j];
-    const float w = x[j + HALF] * r * g[j + HALF];
+    const int i1 = inter ? 2 * j : j, i2 = inter ? 2 * j + 1 : j + HALF;
+    const float u = x[i1] * r * g[i1];
+    const float w = x[i2] * r * g[i2];
     float sn, cs;
     sincosf((float)axis_pos(rope, j, pt, ph, pw) * rope.inv_freq[j], &sn, &cs);
-    x[j] = u * cs - w * sn;
-    x[j + HALF] = w * cs + u * sn;
+    x[i1] = u * cs - w * sn;
+    x[i2] = w * cs + u * sn;
   }
 }
 
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
     const float* src = q + bl * a.qs0 + (tok0 + row) * a.qs1 + head * a.qs2;
     for (int d = 0; d < D; ++d) Qs[t][d] = src[d];
     const int32_t* p3 = a.pos + ((int64_t)bl * Sx + tok0 + row) * 3;
-    prologue_row_f32<D>(Qs[t], a.gq, a.rope, p3[0], p3[1], p3[2], a.eps);
+    prologue_row_f32<D>(Qs[t], a.gq + head * a.gqs, a.rope, p3[0], p3[1], p3[2], a.eps, a.inter);
   }
 
   float o[D];
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(64) void attn_fp32_kernel(Args a) {
         const float* src = k + bl * a.ks0 + (tok0 + n) * a.ks1 + head * a.ks2;
         for (int d = 0; d < D; ++d) Ks[t][d] = src[d];
         const int32_t* p3 = a.pos + ((int64_t)bl * Sx + tok0 + n) * 3;
-        prologue_row_f32<D>(Ks[t], a.gk, a.rope, p3[0], p3[1], p3[2], a.eps);
+        prologue_row_f32<D>(Ks[t], a.gk + head * a.gqs, a.rope, p3[0], p3[1], p3[2], a.eps, a.inter);
       }
     }
     for (int i = t; i < BN * D; i += 64) {

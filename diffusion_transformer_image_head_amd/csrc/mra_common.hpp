@@ -33,8 +33,8 @@ struct Args {
   const void* k;
   const void* v;
   const int32_t* pos;       // [B, S, 3]
-  const float* gq;          // [D]
-  const float* gk;          // [D]
+  const float* gq;          // [D], or [H, D] when gqs == D
+  const float* gk;          // same shape as gq
   const int32_t* seq_lens;  // [B] or null
   const int32_t* cu_seqlens;  // [B + 1] or null: packed sequences (see seq_view)
   void* out;
@@ -52,6 +52,8 @@ struct Args {
   float c2;                 // softmax scale * log2(e)
   float scale;
   float pscale;             // factor applied by k_prologue_kernel before rounding
+  int32_t gqs;              // elements between the gamma rows of two heads (0: shared)
+  int32_t inter;            // rotary pairs (2j, 2j + 1) instead of (j, j + D/2)
   Rope rope;
 };
 

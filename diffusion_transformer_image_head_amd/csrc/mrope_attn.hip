@@ -66,6 +66,8 @@ int check_desc(const mra_desc* d) {
   if (d->dtype == MRA_BF16 && d->kprologue != MRA_KPRO_AUTO && d->kprologue != MRA_KPRO_FUSED &&
       d->kprologue != MRA_KPRO_PREPASS && d->kprologue != MRA_KPRO_NONE)
     return MRA_ERR_PARAM;
+  if (d->rope_pairs != MRA_ROPE_HALF && d->rope_pairs != MRA_ROPE_INTERLEAVED) return MRA_ERR_PARAM;
+  if (d->gamma_per_head != 0 && d->gamma_per_head != 1) return MRA_ERR_PARAM;
   return MRA_OK;
 }
 
@@ -161,6 +163,8 @@ void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const v
   a.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   a.c2 = (float)((double)a.scale * 1.4426950408889634);
   a.pscale = 1.0f;
+  a.gqs = d->gamma_per_head ? d->head_dim : 0;
+  a.inter = d->rope_pairs == MRA_ROPE_INTERLEAVED;
   const int half = d->head_dim / 2;
   for (int j = 0; j < half; ++j)
     a.rope.inv_freq[j] = (float)std::pow((double)d->theta, -2.0 * j / d->head_dim);
@@ -247,7 +251,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 104; }
+int mrope_attn_abi_version(void) { return 105; }
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {
@@ -588,9 +592,17 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
   hipLaunchKernelGGL(mra::bwd_dkdv_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
   hipLaunchKernelGGL(mra::bwd_dq_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-  if (dgamma_q || dgamma_k)
-    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2), dim3(8 * 128), 0, s, (const float*)g.dgq_part,
-                       (const float*)g.dgk_part, p.n_wg, dgamma_q, dgamma_k);
+  if (dgamma_q || dgamma_k) {
+    // per-tile partials are laid out [B, H, n_t, D]: a shared gamma sums all
+    // of them, a per-head gamma sums head h's B * n_t rows
+    const bool ph = d->gamma_per_head;
+    const int n = ph ? d->batch * p.n_t : p.n_wg;
+    const int run = ph ? p.n_t : p.n_wg;
+    const int64_t stride = ph ? (int64_t)d->heads * p.n_t : 0;
+    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2u * (ph ? d->heads : 1)), dim3(8 * 128), 0, s,
+                       (const float*)g.dgq_part, (const float*)g.dgk_part, n, run, stride, dgamma_q,
+                       dgamma_k);
+  }
   return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
@@ -605,6 +617,8 @@ static int qkv_check(const mra_qkv_desc* d) {
   if (!(d->theta > 0.f) || !std::isfinite(d->theta)) return MRA_ERR_PARAM;
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
   if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
+  if (d->rope_pairs != MRA_ROPE_HALF && d->rope_pairs != MRA_ROPE_INTERLEAVED) return MRA_ERR_PARAM;
+  if (d->gamma_per_head != 0 && d->gamma_per_head != 1) return MRA_ERR_PARAM;
   if (d->x_stride < d->hidden || d->x_stride % 8 != 0) return MRA_ERR_STRIDE;
   const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
   for (int i = 0; i < 3; ++i)
@@ -661,6 +675,8 @@ int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, cons
   g.cs = (const float2*)workspace;
   g.gq = gq;
   g.gk = gk;
+  g.gqs = d->gamma_per_head ? d->head_dim : 0;
+  g.inter = d->rope_pairs == MRA_ROPE_INTERLEAVED;
   g.out[0] = (uint16_t*)q_out; g.out[1] = (uint16_t*)k_out; g.out[2] = (uint16_t*)v_out;
   const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
   for (int i = 0; i < 3; ++i) { g.os[i][0] = st[i][0]; g.os[i][1] = st[i][1]; }

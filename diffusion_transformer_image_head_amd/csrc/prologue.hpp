@@ -17,6 +17,10 @@ namespace mra {
 // set) the (cos, sin) table [B, S, D/2]. One wave per token; 16 lanes
 // per head row, so a wave covers 4 heads per step. The token's rotary angles
 // are shared by all heads and computed once per lane with the accurate sincosf.
+// Lane `sub` owns rotary pairs sub*PPL .. +PPL-1: with half-split pairs their
+// elements are the runs [sub*PPL, +PPL) and [D/2 + sub*PPL, +PPL); with
+// interleaved pairs, the one run [2*sub*PPL, +2*PPL). K' keeps the element
+// order of K.
 template <int D>
 __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
   constexpr int HALF = D / 2;
@@ -28,30 +32,56 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
   const int sub = lane & 15, hq = lane >> 4;
   const int32_t* p3 = a.pos + (int64_t)tok * 3;
   const int pt = p3[0], ph = p3[1], pw = p3[2];
+  const bool inter = a.inter;
+  // element offsets of this lane's first and second pair members
+  const int o1 = inter ? 2 * sub * PPL : sub * PPL;
+  const int o2 = inter ? o1 + 1 : o1 + HALF;
 
-  float cs[PPL], sn[PPL], g1[PPL], g2[PPL];
+  float cs[PPL], sn[PPL];
 #pragma unroll
   for (int p = 0; p < PPL; ++p) {
     const int j = sub * PPL + p;
     const float ang = (float)axis_pos(a.rope, j, pt, ph, pw) * a.rope.inv_freq[j];
     sincosf(ang, &sn[p], &cs[p]);
-    g1[p] = a.gk[j];
-    g2[p] = a.gk[j + HALF];
     // the same rotation feeds the Q side inside the attention kernel
     if (hq == 0 && a.cs) a.cs[(int64_t)tok * HALF + j] = make_float2(cs[p], sn[p]);
   }
   const uint16_t* kb = (const uint16_t*)a.k + b * a.ks0 + s * a.ks1;
   for (int h = hq; h < a.H; h += 4) {
-    const uint16_t* src = kb + h * a.ks2 + sub * PPL;
+    const float* gk = a.gk + h * a.gqs;
+    float g1[PPL], g2[PPL];
+    if (inter) {
+      float gv[2 * PPL];
+#pragma unroll
+      for (int i = 0; i < 2 * PPL; i += 4) *(f32x4*)(gv + i) = *(const f32x4*)(gk + o1 + i);
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) { g1[p] = gv[2 * p]; g2[p] = gv[2 * p + 1]; }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) { g1[p] = gk[o1 + p]; g2[p] = gk[o2 + p]; }
+    }
+    const uint16_t* src = kb + h * a.ks2;
     float x1[PPL], x2[PPL];
-    if constexpr (PPL == 4) {
-      const u32x2 w1 = *(const u32x2*)src;
-      const u32x2 w2 = *(const u32x2*)(src + HALF);
+    if (inter) {
+      // PPL pairs = 2 * PPL consecutive elements, first members at even slots
+      uint32_t w[PPL];
+      if constexpr (PPL == 4) {
+        const u32x4 v = *(const u32x4*)(src + o1);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      } else {
+        const u32x2 v = *(const u32x2*)(src + o1);
+        w[0] = v[0]; w[1] = v[1];
+      }
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) { x1[p] = bf16_lo(w[p]); x2[p] = bf16_hi(w[p]); }
+    } else if constexpr (PPL == 4) {
+      const u32x2 w1 = *(const u32x2*)(src + o1);
+      const u32x2 w2 = *(const u32x2*)(src + o2);
       x1[0] = bf16_lo(w1[0]); x1[1] = bf16_hi(w1[0]); x1[2] = bf16_lo(w1[1]); x1[3] = bf16_hi(w1[1]);
       x2[0] = bf16_lo(w2[0]); x2[1] = bf16_hi(w2[0]); x2[2] = bf16_lo(w2[1]); x2[3] = bf16_hi(w2[1]);
     } else {
-      const uint32_t w1 = *(const uint32_t*)src;
-      const uint32_t w2 = *(const uint32_t*)(src + HALF);
+      const uint32_t w1 = *(const uint32_t*)(src + o1);
+      const uint32_t w2 = *(const uint32_t*)(src + o2);
       x1[0] = bf16_lo(w1); x1[1] = bf16_hi(w1);
       x2[0] = bf16_lo(w2); x2[1] = bf16_hi(w2);
     }
@@ -63,27 +93,27 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
     ss += __shfl_xor(ss, 4, 16);
     ss += __shfl_xor(ss, 8, 16);
     const float r = rsqrtf(ss * (1.0f / D) + a.eps) * a.pscale;
-    uint32_t o1[PPL / 2], o2[PPL / 2];
+    float y1[PPL], y2[PPL];
 #pragma unroll
-    for (int p = 0; p < PPL; p += 2) {
-      float y[4];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float u = x1[p + e] * r * g1[p + e];
-        const float w = x2[p + e] * r * g2[p + e];
-        y[e] = u * cs[p + e] - w * sn[p + e];
-        y[2 + e] = w * cs[p + e] + u * sn[p + e];
-      }
-      o1[p / 2] = pack_bf16(y[0], y[1]);
-      o2[p / 2] = pack_bf16(y[2], y[3]);
+    for (int p = 0; p < PPL; ++p) {
+      const float u = x1[p] * r * g1[p];
+      const float w = x2[p] * r * g2[p];
+      y1[p] = u * cs[p] - w * sn[p];
+      y2[p] = w * cs[p] + u * sn[p];
     }
-    uint16_t* dst = a.kp + (((int64_t)b * a.H + h) * a.S + s) * D + sub * PPL;
-    if constexpr (PPL == 4) {
-      *(u32x2*)dst = u32x2{o1[0], o1[1]};
-      *(u32x2*)(dst + HALF) = u32x2{o2[0], o2[1]};
+    uint16_t* dst = a.kp + (((int64_t)b * a.H + h) * a.S + s) * D;
+    if (inter) {
+      if constexpr (PPL == 4)
+        *(u32x4*)(dst + o1) = u32x4{pack_bf16(y1[0], y2[0]), pack_bf16(y1[1], y2[1]),
+                                    pack_bf16(y1[2], y2[2]), pack_bf16(y1[3], y2[3])};
+      else
+        *(u32x2*)(dst + o1) = u32x2{pack_bf16(y1[0], y2[0]), pack_bf16(y1[1], y2[1])};
+    } else if constexpr (PPL == 4) {
+      *(u32x2*)(dst + o1) = u32x2{pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3])};
+      *(u32x2*)(dst + o2) = u32x2{pack_bf16(y2[0], y2[1]), pack_bf16(y2[2], y2[3])};
     } else {
-      *(uint32_t*)dst = o1[0];
-      *(uint32_t*)(dst + HALF) = o2[0];
+      *(uint32_t*)(dst + o1) = pack_bf16(y1[0], y1[1]);
+      *(uint32_t*)(dst + o2) = pack_bf16(y2[0], y2[1]);
     }
   }
 }

@@ -38,6 +38,8 @@ struct QkvArgs {
   uint16_t* out[3];       // q_op, k_op, v: [M, H, D] with (token, head) strides
   int64_t os[3][2];
   int32_t M, hidden, H, n_mt;
+  int32_t gqs;            // elements between two heads' gamma rows (0: shared [D])
+  int32_t inter;          // rotary pairs (2j, 2j + 1) instead of (j, j + D/2)
   float eps, qscale;
 };
 
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(QkvArgs g) {
 
   // ---- epilogue: row scale; Q/K heads: RMSNorm, gamma, rotation (Q: qscale)
   const float* wsc = g.wsc + hb * D;
-  const float* gamma = part == 0 ? g.gq : g.gk;
+  const float* gamma = (part == 0 ? g.gq : g.gk) + head * g.gqs;
   const float qs = part == 0 ? g.qscale : 1.0f;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -200,6 +202,26 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(QkvArgs g) {
       ss = half_swap_sum(ss);
       const float r = rsqrtf(ss * (1.0f / D) + g.eps);
       const float2* csrow = g.cs + (int64_t)min(tok, g.M - 1) * (D / 2);
+      if (g.inter) {
+        // pair j = (2j, 2j + 1): registers e and e + 1 of one lane; the four
+        // dims d0..d0+3 of a register group are pairs d0/2 and d0/2 + 1
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int d0 = db * 32 + gg * 8 + hf * 4;
+            const f32x4 c01 = *(const f32x4*)(csrow + d0 / 2);
+            const f32x4 gv = *(const f32x4*)(gamma + d0);
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const float cs = c01[e], sn = c01[e + 1];
+              const float u = y[db][gg * 4 + e] * r * gv[e];
+              const float w = y[db][gg * 4 + e + 1] * r * gv[e + 1];
+              y[db][gg * 4 + e] = (u * cs - w * sn) * qs;
+              y[db][gg * 4 + e + 1] = (w * cs + u * sn) * qs;
+            }
+          }
+      } else
 #pragma unroll
       for (int db = 0; db < DB / 2; ++db)
 #pragma unroll

@@ -10,9 +10,11 @@
  * and token s of a sequence of S = text_pad + image tokens:
  *
  *   1. RMSNorm over head_dim:  x_hat = x * (mean_d x_d^2 + eps)^-1/2 * gamma
- *      (gamma_q for Q, gamma_k for K; one [head_dim] weight shared by heads);
- *   2. 3D M-RoPE: rotary pair j = (x_hat_j, x_hat_{j+D/2}), j < D/2, is turned
- *      by pos[b,s,axis(j)] * theta^(-2j/D), where axis(j) is t for the first
+ *      (gamma_q for Q, gamma_k for K; one [head_dim] weight shared by heads,
+ *      or one per head with mra_desc.gamma_per_head);
+ *   2. 3D M-RoPE: rotary pair j = (x_hat_j, x_hat_{j+D/2}), j < D/2 (or
+ *      (x_hat_2j, x_hat_2j+1) with mra_desc.rope_pairs = MRA_ROPE_INTERLEAVED),
+ *      is turned by pos[b,s,axis(j)] * theta^(-2j/D), where axis(j) is t for the first
  *      section[0] pairs, h for the next section[1], w for the last section[2]
  *      ("Ideogram 4 deep dive", section 6 part 3 names the split (24,20,20));
  *      the frequency is computed in fp32 (the unsloth commit log for the
@@ -38,8 +40,9 @@
  *    Ideogram 4 checkpoint stores Q/K/V rows stacked in one fused weight, per
  *    the unsloth commit log; Q, K and V have the same head count there).
  *  - pos_thw is [B, S, 3] int32 contiguous, (t, h, w) per token.
- *  - gamma_q, gamma_k are [D] fp32. seq_lens is [B] int32 or NULL (no
- *    padding); values are read on the device and clamped to [0, text_pad].
+ *  - gamma_q, gamma_k are [D] fp32 contiguous ([H, D] with gamma_per_head).
+ *    seq_lens is [B] int32 or NULL (no padding); values are read on the
+ *    device and clamped to [0, text_pad].
  *  - lse, when not NULL, is [B, H, S] fp32 contiguous: natural-log
  *    log-sum-exp of the scaled logits of each valid row, -inf for invalid rows.
  *  - stream is a hipStream_t (NULL = the legacy default stream). Calls are
@@ -68,7 +71,7 @@ typedef enum {
   MRA_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
   MRA_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
   MRA_ERR_HIP = -8,         /* a HIP launch or runtime call failed */
-  MRA_ERR_PARAM = -9        /* theta/eps/scale/kprologue invalid */
+  MRA_ERR_PARAM = -9        /* theta/eps/scale/kprologue/rope_pairs/gamma_per_head invalid */
 } mra_status;
 
 typedef enum { MRA_BF16 = 0, MRA_FP32 = 1 } mra_dtype;
@@ -83,6 +86,13 @@ typedef enum {
                            or rotation is applied; pos_thw, gamma_q, gamma_k are
                            not read and may be NULL */
 } mra_kprologue;
+
+/* Which elements of a head row form rotary pair j. The pages do not say;
+ * both layouts are in use for rotary encodings. */
+typedef enum {
+  MRA_ROPE_HALF = 0,        /* (j, j + D/2): the rotate-half layout (default) */
+  MRA_ROPE_INTERLEAVED = 1  /* (2j, 2j + 1) */
+} mra_rope_pairs;
 
 typedef struct {
   int32_t batch;          /* B >= 0 (0 = nothing to do) */
@@ -100,6 +110,8 @@ typedef struct {
   int64_t k_stride[3];
   int64_t v_stride[3];
   int64_t o_stride[3];
+  int32_t rope_pairs;     /* mra_rope_pairs */
+  int32_t gamma_per_head; /* 0: gamma_q, gamma_k are [D]; 1: [H, D] (row h for head h) */
 } mra_desc;
 
 /* Host-only check of a call's arguments; touches no device and reads no
@@ -211,8 +223,10 @@ int mrope_attn_fwd_varlen(const mra_desc* desc, const void* q, const void* k, co
  * the forward's out and lse (mrope_attn_fwd with a non-NULL lse) and the
  * upstream gradient dout, writes dq, dk, dv (the gradients of sum(dout * out)
  * w.r.t. q, k, v; zero rows for padded text slots) and, when not NULL,
- * dgamma_q and dgamma_k ([D] fp32, summed over every valid row and head; the
- * sum runs in a fixed order, so results are reproducible). bf16 with
+ * dgamma_q and dgamma_k (fp32 with gamma's shape: [D] summed over every
+ * valid row and head, or with gamma_per_head [H, D] with row h summed over
+ * head h's valid rows; the sums run in a fixed order, so results are
+ * reproducible). bf16 with
  * head_dim 128 only (else MRA_ERR_UNSUPPORTED). dout has out's strides
  * (o_stride); dq, dk, dv have q's, k's and v's strides; all four must be
  * 16-byte aligned and must not overlap the inputs or each other. The packed
@@ -255,6 +269,8 @@ typedef struct {
   int64_t q_stride[2];    /* token, head strides of q_out (elements) */
   int64_t k_stride[2];
   int64_t v_stride[2];
+  int32_t rope_pairs;     /* mra_rope_pairs */
+  int32_t gamma_per_head; /* 0: gamma_q, gamma_k are [D]; 1: [H, D] */
 } mra_qkv_desc;
 
 size_t mrope_qkv_proj_workspace_size(const mra_qkv_desc* desc);

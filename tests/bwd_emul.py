@@ -43,7 +43,7 @@ def emulate(w, do):
             dqr[b, :, h] = scale * ds @ k2[b, kv, h]
             dkr[b, kv, h] = np.log(2) * ds.T @ q2[b, :, h]
     c, s = _angles(w.pos, w.section, d_, w.theta)
-    dxq = _rotate(dqr, c, s, -1.0); dxk = _rotate(dkr, c, s, -1.0)
+    dxq = _rotate(dqr, c, s, -1.0, "half"); dxk = _rotate(dkr, c, s, -1.0, "half")
     def nb(x, g, dxh):
         r = 1 / np.sqrt(np.mean(x * x, -1, keepdims=True) + w.eps)
         dg = np.sum(dxh * x * r, axis=(0, 1, 2))

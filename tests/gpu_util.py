@@ -33,6 +33,7 @@ def run_gpu(w, dev=None, **kw):
     import torch
     from diffusion_transformer_image_head_amd.binding import mrope_attn
     dev = dev or to_dev(w)
+    kw.setdefault("rope_pairs", w.rope_pairs)
     out, lse = mrope_attn(dev["q"], dev["k"], dev["v"], dev["pos"], dev["gamma_q"],
                           dev["gamma_k"], dev["seq_lens"], text_pad=w.text_pad,
                           section=w.section, theta=w.theta, eps=w.eps, return_lse=True, **kw)
@@ -43,7 +44,7 @@ def run_gpu(w, dev=None, **kw):
 def run_oracle(w, rows=None, heads=None):
     return oracle_fwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens,
                       text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
-                      rows=rows, heads=heads)
+                      rows=rows, heads=heads, rope_pairs=w.rope_pairs)
 
 
 def errors(got, ref):

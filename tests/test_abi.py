@@ -53,19 +53,32 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name)
 
 
-def test_problem_layout_matches_header(lib):
-    assert ctypes.sizeof(B.Problem) == 9 * 8
-    assert B.Problem.out.offset == 56
+def _c_layout(tmp_path, struct, fields):
+    """sizeof and offsetof of a header struct, from a C program built with gcc."""
+    src = tmp_path / f"{struct}.c"
+    lines = [f'#include "{HEADER}"', "#include <stdio.h>", "#include <stddef.h>", "int main(void) {",
+             f'  printf("%zu\\n", sizeof({struct}));']
+    lines += [f'  printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / struct
+    subprocess.run(["gcc", "-std=c11", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    return [int(x) for x in out]
 
 
-def test_desc_layout_matches_header(lib):
-    # 11 int32/float fields + 3 + 12 int64 strides; int64 block aligned at 8
-    assert ctypes.sizeof(B.Desc) == 4 * 13 + 4 + 8 * 12
-    assert B.Desc.q_stride.offset == 56
+@pytest.mark.parametrize("cls,struct", [(B.Desc, "mra_desc"), (B.QkvDesc, "mra_qkv_desc"),
+                                        (B.Problem, "mra_problem")])
+def test_struct_layouts_match_header(tmp_path, cls, struct):
+    names = [f[0] for f in cls._fields_]
+    got = _c_layout(tmp_path, struct, names)
+    assert ctypes.sizeof(cls) == got[0]
+    for name, off in zip(names, got[1:]):
+        assert getattr(cls, name).offset == off, name
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 104
+    assert lib.mrope_attn_abi_version() == 105
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -92,6 +105,7 @@ def test_validate_accepts_good_calls(lib):
     assert val(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
     assert val(desc(text_pad=0)) == 0
     assert val(desc(text_pad=100)) == 0
+    assert val(desc(rope_pairs="interleaved", gamma_per_head=True)) == 0
     assert val(desc(), seq=FAKE) == 0
     # strided views of one fused [B, S, 3, H, D] qkv buffer
     st = (100 * 3 * 4 * 128, 3 * 4 * 128, 128)
@@ -113,6 +127,8 @@ def test_validate_accepts_good_calls(lib):
     (dict(eps=-1e-6), -9),
     (dict(scale=float("inf")), -9),
     (dict(kprologue=5), -9),
+    (dict(rope_pairs=2), -9),
+    (dict(gamma_per_head=2), -9),
     (dict(q_stride=(100 * 4 * 128, 4 * 128, 100)), -5),     # bf16 needs multiples of 8
     (dict(o_stride=(-1, 4 * 128, 128)), -5),
     (dict(seq=1 << 20, text_pad=0, k_stride=(0, 1 << 11, 128)), -6),   # > 2 GiB per slice

@@ -31,7 +31,8 @@ def run_bwd(w, do, dev=None):
     import torch
     from diffusion_transformer_image_head_amd.binding import mrope_attn, mrope_attn_bwd
     dev = dev or to_dev(w)
-    kw = dict(text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps)
+    kw = dict(text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
+              rope_pairs=w.rope_pairs)
     out, lse = mrope_attn(dev["q"], dev["k"], dev["v"], dev["pos"], dev["gamma_q"], dev["gamma_k"],
                           dev["seq_lens"], return_lse=True, **kw)
     dot = torch.from_numpy(do).cuda().to(torch.bfloat16)
@@ -80,6 +81,24 @@ def test_bwd_small(name):
         for b, l in enumerate(w.seq_lens):
             for t in got[:3]:
                 assert np.all(t[b, int(l):w.text_pad] == 0)
+
+
+@pytest.mark.parametrize("per_head,pairs", [(True, "half"), (False, "interleaved"),
+                                            (True, "interleaved")])
+@pytest.mark.parametrize("name", ["ragged157", "multi_tile"])
+def test_bwd_conventions(name, per_head, pairs):
+    """A gamma per head (its gradient per head, [H, D]) and interleaved
+    rotary pairs, every output compared with the oracle."""
+    say(f"case: bwd {name} gamma_per_head={per_head} rope_pairs={pairs}")
+    w = make_workload(**SMALL[name], dtype="bf16", seed=730 + list(SMALL).index(name),
+                      gamma_per_head=per_head, rope_pairs=pairs)
+    do = dout_for(w)
+    got = run_bwd(w, do)
+    ref = oracle_bwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens, do,
+                     text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
+                     rope_pairs=pairs)
+    assert got[3].shape == ref[3].shape and got[4].shape == ref[4].shape
+    check_bwd(got, ref, f"{name} {per_head} {pairs}")
 
 
 def test_bwd_poisoned_padding_is_invisible():

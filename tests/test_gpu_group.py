@@ -28,7 +28,8 @@ def run_group(ws, **kw):
     probs = []
     for w in ws:
         d = to_dev(w)
-        probs.append(dict(d, text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps))
+        probs.append(dict(d, text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps,
+                          rope_pairs=w.rope_pairs))
     res = mrope_attn_group(probs, return_lse=True, **kw)
     torch.cuda.synchronize()
     return [(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64))
@@ -76,6 +77,25 @@ def test_group_of_four_mixed_shapes():
         if w.seq_lens is not None:
             for b, l in enumerate(w.seq_lens):
                 assert np.all(out[b, int(l):w.text_pad] == 0)
+
+
+@pytest.mark.parametrize("kpro", ["prepass", "fused"])
+def test_group_mixed_conventions(kpro):
+    """Members with different conventions in one launch: each keeps its own
+    gamma shape and rotary pair layout."""
+    say(f"case: group mixed conventions kprologue={kpro}")
+    ws = [
+        make_workload(2, 3, 128, (16, 24, 24), 40, 9, 13, text_lens=(17, 40), dtype="bf16", seed=440,
+                      gamma_per_head=True, rope_pairs="interleaved"),
+        make_workload(1, 2, 128, (16, 24, 24), 0, 10, 11, dtype="bf16", seed=441),
+        make_workload(1, 4, 128, (24, 20, 20), 30, 8, 8, text_lens=(9,), dtype="bf16", seed=442,
+                      rope_pairs="interleaved"),
+    ]
+    got = run_group(ws, kprologue=kpro)
+    for i, (w, (out, lse)) in enumerate(zip(ws, got)):
+        ref, rlse = run_oracle(w)
+        check_parity(out, ref, "bf16", f"member {i} {w.shape} {w.rope_pairs}")
+        check_lse(lse, rlse)
 
 
 def test_group_d64_and_empty_member():

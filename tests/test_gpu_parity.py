@@ -111,6 +111,44 @@ def test_bf16_peaked():
     assert ma <= PEAKED_BARS[0] and rr <= PEAKED_BARS[1]
 
 
+# ------------------------------------------------------------------ conventions
+# a gamma per head ([H, D]) and interleaved rotary pairs (2j, 2j + 1), alone
+# and together, on multi-tile ragged shapes, D = 64, and the fp32 path
+CONV = [(True, "half"), (False, "interleaved"), (True, "interleaved")]
+
+
+@pytest.mark.parametrize("kpro", KPRO)
+@pytest.mark.parametrize("per_head,pairs", CONV)
+@pytest.mark.parametrize("name", ["ragged157", "multi_tile", "d64"])
+def test_bf16_conventions(name, per_head, pairs, kpro):
+    say(f"case: bf16 {name} gamma_per_head={per_head} rope_pairs={pairs} kprologue={kpro}")
+    w = make_workload(**SMALL[name], dtype="bf16", seed=350 + list(SMALL).index(name),
+                      gamma_per_head=per_head, rope_pairs=pairs)
+    _full_check(w, kprologue=kpro)
+
+
+@pytest.mark.parametrize("per_head,pairs", CONV)
+@pytest.mark.parametrize("d,sec", [(128, (16, 24, 24)), (64, (8, 12, 12))])
+def test_fp32_conventions(d, sec, per_head, pairs):
+    say(f"case: fp32 D={d} gamma_per_head={per_head} rope_pairs={pairs}")
+    _full_check(make_workload(2, 3, d, sec, 12, 5, 6, text_lens=(4, 12), dtype="fp32", seed=360,
+                              gamma_per_head=per_head, rope_pairs=pairs))
+
+
+def test_conventions_change_the_result():
+    """The layouts and gamma rows reach the kernel: each choice changes the
+    output (compared with the default conventions on the same values)."""
+    say("case: conventions are not ignored")
+    w = make_workload(**SMALL["ragged157"], dtype="bf16", seed=370, gamma_per_head=True)
+    a, _ = run_gpu(w, rope_pairs="half")
+    b, _ = run_gpu(w, rope_pairs="interleaved")
+    assert np.max(np.abs(a - b)) > 0.05
+    w2 = make_workload(**SMALL["ragged157"], dtype="bf16", seed=370, gamma_per_head=True)
+    w2.gamma_q = np.ascontiguousarray(w2.gamma_q[::-1])   # permute the heads' rows
+    c, _ = run_gpu(w2, rope_pairs="half")
+    assert np.max(np.abs(a - c)) > 0.05
+
+
 def test_prepass_and_fused_agree():
     say("case: prepass vs fused K prologue")
     w = make_workload(**SMALL["multi_tile"], dtype="bf16", seed=330)
@@ -196,7 +234,7 @@ def test_config_512px_full():
     _full_check(config_workload("512px"))
 
 
-@pytest.mark.parametrize("name", ["1024px", "ragged", "long", "h36", "2048px"])
+@pytest.mark.parametrize("name", ["1024px", "ragged", "long", "h36", "2048px", "conv"])
 def test_config_sampled_rows(name):
     say(f"case: {name} config, sampled rows")
     w = config_workload(name)

@@ -38,7 +38,7 @@ def run_proj(w):
     from diffusion_transformer_image_head_amd.binding import mrope_qkv_proj
     d = to_dev(w)
     outs = mrope_qkv_proj(d["x"], d["w8"], d["w_scale"], d["pos"], d["gamma_q"], d["gamma_k"],
-                          heads=w.heads, section=w.section)
+                          heads=w.heads, section=w.section, rope_pairs=w.rope_pairs)
     torch.cuda.synchronize()
     return outs, [o.float().cpu().numpy().astype(np.float64) for o in outs]
 
@@ -66,6 +66,18 @@ def test_qkv_small(shape):
     ref = oracle_qkv_proj(w.x, w.w8, w.w_scale, w.pos, w.gamma_q, w.gamma_k, heads=h, head_dim=128,
                           section=w.section, qscale=qscale())
     check_proj(got, ref, f"{shape}")
+
+
+@pytest.mark.parametrize("per_head,pairs", [(True, "half"), (False, "interleaved"),
+                                            (True, "interleaved")])
+def test_qkv_conventions(per_head, pairs):
+    say(f"case: qkv gamma_per_head={per_head} rope_pairs={pairs}")
+    w = make_qkv_workload(2, 3, 128, (16, 24, 24), 40, 5, 7, 128, seed=830, gamma_per_head=per_head,
+                          rope_pairs=pairs)
+    _, got = run_proj(w)
+    ref = oracle_qkv_proj(w.x, w.w8, w.w_scale, w.pos, w.gamma_q, w.gamma_k, heads=3, head_dim=128,
+                          section=w.section, qscale=qscale(), rope_pairs=pairs)
+    check_proj(got, ref, f"{per_head} {pairs}")
 
 
 def test_qkv_1024px_sampled_rows():

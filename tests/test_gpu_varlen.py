@@ -36,14 +36,15 @@ def run_varlen(w, max_seqlen=None, out=None, **kw):
     d = to_dev(w)
     o, l = mrope_attn_varlen(d["q"], d["k"], d["v"], d["pos"], d["gamma_q"], d["gamma_k"], d["cu"],
                              w.max_seqlen if max_seqlen is None else max_seqlen,
-                             section=w.section, return_lse=True, out=out, **kw)
+                             section=w.section, return_lse=True, out=out,
+                             rope_pairs=w.rope_pairs, **kw)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64)
 
 
 def oracle(w):
     return oracle_fwd_varlen(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens,
-                             section=w.section, theta=w.theta, eps=w.eps)
+                             section=w.section, theta=w.theta, eps=w.eps, rope_pairs=w.rope_pairs)
 
 
 @pytest.mark.parametrize("kpro", ["prepass", "fused"])
@@ -54,6 +55,17 @@ def test_varlen_small_bf16(kpro):
     out, lse = run_varlen(w, kprologue=kpro)
     ref, rlse = oracle(w)
     check_parity(out, ref, "bf16", f"varlen {w.q.shape} cu={w.cu_seqlens.tolist()}")
+    check_lse(lse, rlse)
+
+
+@pytest.mark.parametrize("kpro", ["prepass", "fused"])
+def test_varlen_conventions(kpro):
+    say(f"case: varlen gamma per head + interleaved pairs kprologue={kpro}")
+    w = make_varlen_workload(3, 128, (16, 24, 24), text_lens=(17, 0, 40), grids=((9, 13), (7, 7), (10, 12)),
+                             seed=510, gamma_per_head=True, rope_pairs="interleaved")
+    out, lse = run_varlen(w, kprologue=kpro)
+    ref, rlse = oracle(w)
+    check_parity(out, ref, "bf16", f"varlen conventions cu={w.cu_seqlens.tolist()}")
     check_lse(lse, rlse)
 
 
