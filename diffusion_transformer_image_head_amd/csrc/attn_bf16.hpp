@@ -26,10 +26,11 @@
 // a load lands at 16*L of a 1 KiB run), with 16-byte chunks XOR-swizzled per
 // row so the matrix-operand reads are free of bank conflicts. K' rows sit in
 // the order that makes each lane's 16 S^T values 16 consecutive keys, so the P
-// fragment feeds P.V directly. K' and V are double-buffered and staggered by
-// one tile: after each tile's barrier the loads of K'(t+2) and V(t+1) are
-// issued, then Q.K'(t+1) is issued before the softmax of tile t so the matrix
-// cores run while the vector ALUs do the exponentials.
+// fragment feeds P.V directly. K' and V are double-buffered: after each
+// tile's barrier the loads of tile t+1 are issued, then Q.K'(t), the softmax
+// and P.V(t) run; the two waves sharing a SIMD (two workgroups per CU) overlap
+// one's matrix work with the other's exponentials, and a wave raises its issue
+// priority for its P.V run.
 //
 // Numerics: Q' is rounded to bf16 already multiplied by softmax_scale*log2(e),
 // so S^T is in log2 units; the S^T accumulators start at -m (the running row
@@ -115,7 +116,7 @@ __device__ __forceinline__ float* part_record(float* part, int nsplit, int st, i
 // Q' made here from q; 1: both made here (K while its tile is staged);
 // 2: q and k already hold the operands Q'' (scaled by c2) and K'.
 template <int D, int WAVES, int BN, int RB, int KPM, int G>
-__global__ __launch_bounds__(WAVES * 64, RB == 1 ? 2 : 1) void attn_bf16_kernel(Group<G> gp) {
+__global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16_kernel(Group<G> gp) {
   constexpr bool KFUSED = KPM == 1, PRE = KPM == 2;
   constexpr int BM = WAVES * 32 * RB;
   constexpr int NT = WAVES * 64;

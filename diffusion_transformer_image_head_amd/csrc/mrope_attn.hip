@@ -17,7 +17,10 @@ namespace {
 
 using mra::Args;
 
-constexpr int kWaves = 4;
+#ifndef MRA_WAVES
+#define MRA_WAVES 4
+#endif
+constexpr int kWaves = MRA_WAVES;
 #ifndef MRA_BLOCK_N
 #define MRA_BLOCK_N 64
 #endif
@@ -31,7 +34,7 @@ constexpr int kFp32BlockM = 64;
 constexpr size_t kWsAlign = 256;
 // Attention workgroups resident at once on an MI355X (256 CUs, two per CU).
 constexpr int kComputeUnits = 256;
-constexpr int kResidentSlots = kComputeUnits * (kRowBlocks == 1 ? 2 : 1);
+constexpr int kResidentSlots = kComputeUnits * (kWaves * kRowBlocks >= 8 ? 1 : 2);
 // Workgroups the split tiles of the last wave are spread over: one per CU
 // (measured faster than filling both slots of every CU, which doubles the
 // partial results the merge pass reads).
