@@ -32,12 +32,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "diffusion_transformer_image_head_amd", "csrc")
 
 
+# sources the forward attention's kernels and launches are built from
+FORWARD_SOURCES = ("attn_bf16.hpp", "mra_common.hpp", "mrope_attn.hip", "prologue.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 

@@ -94,16 +94,17 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs g) {
 // j + D/2 in db and db + D/64, or (inter) 2j and 2j + 1 in r and r + 1.
 // Writes the bf16 input gradient of the row to dst (if in_seq; zeros for an
 // invalid row) and returns this lane's gamma gradient contributions in dg
-// (zero for an invalid row).
-template <int D>
+// (zero for an invalid row). INTER is a template parameter: a runtime choice
+// keeps both rotations' values live and the dK/dV kernel spills.
+template <int D, bool INTER>
 __device__ __forceinline__ void rope_rms_bwd(const f32x16 (&acc)[D / 32], float mult,
                                              const uint16_t* xrow, const float* gamma,
                                              const float2* csrow, float eps, bool valid,
-                                             bool in_seq, uint16_t* dst, int hf, bool inter,
+                                             bool in_seq, uint16_t* dst, int hf,
                                              float (&dg)[D / 32][16]) {
   constexpr int DB = D / 32, HB = DB / 2;
   float dx[DB][16], x[DB][16];
-  if (inter) {
+  if constexpr (INTER) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -209,8 +210,9 @@ __device__ __forceinline__ void dgamma_partial(float (&dg)[D / 32][16], float* r
 }
 
 // dK and dV: one workgroup per (batch, head, 128 keys), 32 keys per wave;
-// query tiles of 32 stream through double-buffered LDS.
-template <int D>
+// query tiles of 32 stream through double-buffered LDS. INTER: interleaved
+// rotary pairs (2j, 2j + 1) in the epilogue's inverse rotation.
+template <int D, bool INTER>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   constexpr int KC = D / 16, DB = D / 32, BQ = 32, TILEB = BQ * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
@@ -455,15 +457,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     const uint16_t* xrow = (const uint16_t*)a.k + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
     const float2* csrow = a.cs + ((int64_t)b * S + kc) * (D / 2);
     uint16_t* dst = (uint16_t*)g.dk + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
-    rope_rms_bwd<D>(dkacc, kLn2, xrow, a.gk + head * a.gqs, csrow, a.eps, kvalid, kin, dst, hf,
-                    a.inter, dg);
+    rope_rms_bwd<D, INTER>(dkacc, kLn2, xrow, a.gk + head * a.gqs, csrow, a.eps, kvalid, kin, dst,
+                           hf, dg);
   }
   dgamma_partial<D>(dg, red, g.dgk_part + (int64_t)tile * D, wave, lane);
 }
 
 // dQ: one workgroup per (batch, head, 128 queries), 32 per wave; key tiles of
-// 32 (K' and V) stream through double-buffered LDS.
-template <int D>
+// 32 (K' and V) stream through double-buffered LDS. INTER as for dK/dV.
+template <int D, bool INTER>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
   constexpr int KC = D / 16, DB = D / 32, BK = 32, TILEB = BK * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
@@ -612,8 +614,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
     const uint16_t* xrow = (const uint16_t*)a.q + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
     const float2* csrow = a.cs + ((int64_t)b * S + qc) * (D / 2);
     uint16_t* dst = (uint16_t*)g.dq + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
-    rope_rms_bwd<D>(dqacc, a.scale, xrow, a.gq + head * a.gqs, csrow, a.eps, qvalid, qin, dst, hf,
-                    a.inter, dg);
+    rope_rms_bwd<D, INTER>(dqacc, a.scale, xrow, a.gq + head * a.gqs, csrow, a.eps, qvalid, qin, dst,
+                           hf, dg);
   }
   dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)tile * D, wave, lane);
 }
@@ -637,7 +639,11 @@ __global__ __launch_bounds__(8 * D) void bwd_dgamma_kernel(const float* part_q, 
   if (!out) return;
   out += (int64_t)h * D;
   const int d = threadIdx.x % D, grp = threadIdx.x / D;
-  auto at = [&](int i) { return part[((int64_t)(i / run) * stride + i % run) * D + d]; };
+  // a shared gamma sums every partial in order (run == n: no division)
+  auto at = [&](int i) {
+    const int64_t r = run == n ? i : (int64_t)(i / run) * stride + i % run;
+    return part[r * D + d];
+  };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int i = grp;
   for (; i + 24 < n; i += 32) {

@@ -593,8 +593,13 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, aq);
   const int64_t rows = tokens * d->heads;
   hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
-  hipLaunchKernelGGL(mra::bwd_dkdv_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-  hipLaunchKernelGGL(mra::bwd_dq_kernel<128>, dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+  if (g.a.inter) {
+    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+  }
   if (dgamma_q || dgamma_k) {
     // per-tile partials are laid out [B, H, n_t, D]: a shared gamma sums all
     // of them, a per-head gamma sums head h's B * n_t rows

@@ -1,0 +1,67 @@
+"""Register budgets of the HIP kernels, checked on the CPU from the device
+assembly the compiler writes for gfx950 (no GPU needed).
+
+A kernel that spills, or a 4-wave attention kernel that needs more than 256
+VGPRs (so only one workgroup fits per CU instead of two), still computes the
+right result, so no parity test notices it; only its speed collapses. These
+ceilings catch that at build time.
+"""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from diffusion_transformer_image_head_amd import build as B
+
+# spill ceilings by kernel; every kernel not named here must not spill. The
+# dK/dV kernel holds dK, dV, K' and a four-stage pipeline at one wave per
+# SIMD, at the 512-register limit, and spills a few registers outside its loop.
+SPILL_CEILING = {"bwd_dkdv_kernel": 8}
+# two attention workgroups per CU need each wave within 256 registers
+VGPR_CEILING = {"attn_bf16_kernel": 256, "bwd_dq_kernel": 256, "qkv_proj_kernel": 256}
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm") / "mrope_attn.s"
+    flags = [f for f in B.flags() if f not in ("-shared", "-fPIC")]
+    cmd = [B.hipcc()] + flags + ["--cuda-device-only", "-S",
+                                 os.path.join(B.CSRC, "mrope_attn.hip"), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    text = out.read_text()
+    meta = text[text.index("amdhsa.kernels:"):]
+    res = {}
+    for ent in meta.split("\n  - ")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", ent)
+        if not name:
+            continue
+        res[name.group(1)] = (int(re.search(r"\.vgpr_count:\s+(\d+)", ent).group(1)),
+                              int(re.search(r"\.vgpr_spill_count:\s+(\d+)", ent).group(1)))
+    return res
+
+
+def _kind(mangled):
+    m = re.match(r"_ZN3mra\d+(\w+?)I", mangled)
+    return m.group(1) if m else mangled
+
+
+def test_every_kernel_is_reported(kernels):
+    kinds = {_kind(k) for k in kernels}
+    for k in ("attn_bf16_kernel", "split_merge_kernel", "k_prologue_kernel", "rope_table_kernel",
+              "attn_fp32_kernel", "bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
+              "bwd_dgamma_kernel", "qkv_proj_kernel"):
+        assert k in kinds, k
+
+
+def test_spills_within_ceiling(kernels):
+    for name, (vgpr, spill) in kernels.items():
+        assert spill <= SPILL_CEILING.get(_kind(name), 0), (name, vgpr, spill)
+
+
+def test_occupancy_register_budgets(kernels):
+    for name, (vgpr, _) in kernels.items():
+        ceiling = VGPR_CEILING.get(_kind(name))
+        if ceiling is not None:
+            assert vgpr <= ceiling, (name, vgpr)
