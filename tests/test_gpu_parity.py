@@ -246,3 +246,27 @@ def test_config_sampled_rows(name):
     if w.seq_lens is not None:
         for b, l in enumerate(w.seq_lens):
             assert np.all(out[b, int(l):w.text_pad] == 0)
+
+
+def test_max_sequence_sampled():
+    """The longest sequence the ABI takes for 32 heads of 128 in a contiguous
+    [B, S, H, D] layout: byte offsets inside one (batch, head) slice must stay
+    below 2^31, so S * 32 * 128 * 2 + 256 < 2^31, S <= 262143. Here 512 text
+    slots (300 real) + a 510 x 512 image = 261,632 tokens; one more image row
+    is rejected by the host check. Sampled rows of two heads are compared with
+    the oracle run on those two heads alone (heads are independent)."""
+    from diffusion_transformer_image_head_amd import binding as B
+    say("case: max sequence 261632 tokens, sampled rows of heads 0 and 31")
+    d = B.make_desc(1, 512 + 511 * 512, 32, 128, text_pad=512)
+    assert B.validate(d, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, 0x10000, None, 0x10000) == -6
+    w = make_workload(1, 32, 128, (16, 24, 24), 512, 510, 512, text_lens=(300,), dtype="bf16", seed=380)
+    out, lse = run_gpu(w)
+    heads = [0, 31]
+    rows = sample_rows(w, n=48, seed=1)
+    for f in ("q", "k", "v"):
+        setattr(w, f, np.ascontiguousarray(getattr(w, f)[:, :, heads]))
+    ref, rlse = run_oracle(w, rows=rows)
+    check_parity(out[:, rows][:, :, heads], ref, "bf16", f"max sequence rows={len(rows)}")
+    check_lse(lse[:, heads][:, :, rows], rlse)
+    assert np.all(out[0, 300:512] == 0)
+
