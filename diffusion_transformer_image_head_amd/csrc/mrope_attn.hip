@@ -511,192 +511,8 @@ int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const
   return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 
-// ---- backward pass ---------------------------------------------------------
-// Workspace: (cos, sin) table [B, S, D/2] float2, K' and Q'' [B, H, S, D] bf16,
-// (l2, D) pairs [B, H, S, 2] fp32, then the gamma partials of the dq and dk/dv
-// workgroups [n_wg, D] fp32 each; every piece 256-byte aligned.
-struct BwdPlan {
-  int n_t, n_wg;
-  size_t off_cs, off_kp, off_qp, off_ld, off_gq, off_gk, bytes;
-};
-
-static BwdPlan bwd_plan(const mra_desc* d) {
-  BwdPlan p;
-  const size_t rows = (size_t)d->batch * d->seq * d->heads;
-  p.n_t = (d->seq + 127) / 128;
-  p.n_wg = d->batch * d->heads * p.n_t;
-  size_t off = 0;
-  p.off_cs = off; off += table_bytes(d);
-  p.off_kp = off; off += round_up(rows * d->head_dim * 2, kWsAlign);
-  p.off_qp = off; off += round_up(rows * d->head_dim * 2, kWsAlign);
-  p.off_ld = off; off += round_up(rows * 8, kWsAlign);
-  p.off_gq = off; off += round_up((size_t)p.n_wg * d->head_dim * 4, kWsAlign);
-  p.off_gk = off; off += round_up((size_t)p.n_wg * d->head_dim * 4, kWsAlign);
-  p.bytes = off;
-  return p;
-}
-
-static int bwd_check(const mra_desc* d) {
-  int rc = check_desc(d);
-  if (rc != MRA_OK) return rc;
-  if (d->dtype != MRA_BF16 || d->head_dim != 128) return MRA_ERR_UNSUPPORTED;
-  if (d->kprologue == MRA_KPRO_NONE) return MRA_ERR_UNSUPPORTED;
-  return MRA_OK;
-}
-
-size_t mrope_attn_bwd_workspace_size(const mra_desc* d) {
-  if (bwd_check(d) != MRA_OK || d->batch == 0 || d->seq == 0) return 0;
-  return bwd_plan(d).bytes;
-}
-
-int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* v,
-                   const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
-                   const void* out, const float* lse, const void* dout, void* dq, void* dk,
-                   void* dv, float* dgamma_q, float* dgamma_k, void* workspace, size_t ws_bytes,
-                   void* stream) {
-  int rc = bwd_check(d);
-  if (rc != MRA_OK) return rc;
-  rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
-  if (rc != MRA_OK) return rc;
-  if (d->batch == 0 || d->seq == 0) return MRA_OK;
-  if (!lse || !dout || !dq || !dk || !dv) return MRA_ERR_NULL;
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MRA_ERR_STRIDE;
-  if (!aligned(lse, 4) || !aligned(dgamma_q, 4) || !aligned(dgamma_k, 4)) return MRA_ERR_STRIDE;
-  const BwdPlan p = bwd_plan(d);
-  if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
-  const char* fi = std::getenv("MRA_FAULT_INJECT");
-  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
-
-  char* w = (char*)workspace;
-  mra::BwdArgs g;
-  std::memset(&g, 0, sizeof(g));
-  fill_args(g.a, d, q, k, v, pos, gq, gk, seq_lens, (void*)out, (float*)lse);
-  g.a.cs = (float2*)(w + p.off_cs);
-  g.a.kp = (uint16_t*)(w + p.off_kp);
-  g.dout = dout;
-  g.ds0 = d->o_stride[0]; g.ds1 = d->o_stride[1]; g.ds2 = d->o_stride[2];
-  g.dq = dq; g.dk = dk; g.dv = dv;
-  g.qp = (const uint16_t*)(w + p.off_qp);
-  g.ld = (float*)(w + p.off_ld);
-  g.dgq_part = (float*)(w + p.off_gq);
-  g.dgk_part = (float*)(w + p.off_gk);
-  g.dgq = dgamma_q; g.dgk = dgamma_k;
-  g.n_t = p.n_t;
-
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t tokens = (int64_t)d->batch * d->seq;
-  // K' and the rotary table, then Q'' = c2 * rope(rmsnorm(q)) (same kernel)
-  hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, g.a);
-  Args aq = g.a;
-  aq.k = q; aq.ks0 = aq.qs0; aq.ks1 = aq.qs1; aq.ks2 = aq.qs2;
-  aq.gk = gq; aq.kp = (uint16_t*)g.qp; aq.cs = nullptr; aq.pscale = aq.c2;
-  hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, aq);
-  const int64_t rows = tokens * d->heads;
-  hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
-  if (g.a.inter) {
-    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-  } else {
-    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-  }
-  if (dgamma_q || dgamma_k) {
-    // per-tile partials are laid out [B, H, n_t, D]: a shared gamma sums all
-    // of them, a per-head gamma sums head h's B * n_t rows
-    const bool ph = d->gamma_per_head;
-    const int n = ph ? d->batch * p.n_t : p.n_wg;
-    const int run = ph ? p.n_t : p.n_wg;
-    const int64_t stride = ph ? (int64_t)d->heads * p.n_t : 0;
-    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2u * (ph ? d->heads : 1)), dim3(8 * 128), 0, s,
-                       (const float*)g.dgq_part, (const float*)g.dgk_part, n, run, stride, dgamma_q,
-                       dgamma_k);
-  }
-  return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
-}
-
-// ---- fp8 QKV projection --------------------------------------------------
-static int qkv_check(const mra_qkv_desc* d) {
-  if (!d) return MRA_ERR_NULL;
-  if (d->tokens < 0 || d->heads < 1 || d->hidden <= 0 || d->hidden % 64 != 0) return MRA_ERR_SHAPE;
-  if (d->head_dim != 128) return MRA_ERR_UNSUPPORTED;
-  if (d->section[0] < 0 || d->section[1] < 0 || d->section[2] < 0 ||
-      (int64_t)d->section[0] + d->section[1] + d->section[2] != d->head_dim / 2)
-    return MRA_ERR_SECTION;
-  if (!(d->theta > 0.f) || !std::isfinite(d->theta)) return MRA_ERR_PARAM;
-  if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
-  if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
-  if (d->rope_pairs != MRA_ROPE_HALF && d->rope_pairs != MRA_ROPE_INTERLEAVED) return MRA_ERR_PARAM;
-  if (d->gamma_per_head != 0 && d->gamma_per_head != 1) return MRA_ERR_PARAM;
-  if (d->x_stride < d->hidden || d->x_stride % 8 != 0) return MRA_ERR_STRIDE;
-  const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
-  for (int i = 0; i < 3; ++i)
-    if (st[i][0] < 0 || st[i][1] < 0 || st[i][0] % 8 != 0 || st[i][1] % 8 != 0) return MRA_ERR_STRIDE;
-  // 32-bit byte offsets inside x and each weight block
-  if ((int64_t)d->tokens * d->x_stride * 2 >= ((int64_t)1 << 31)) return MRA_ERR_UNSUPPORTED;
-  if ((int64_t)d->head_dim * d->hidden >= ((int64_t)1 << 31)) return MRA_ERR_UNSUPPORTED;
-  return MRA_OK;
-}
-
-size_t mrope_qkv_proj_workspace_size(const mra_qkv_desc* d) {
-  if (qkv_check(d) != MRA_OK || d->tokens == 0) return 0;
-  return round_up((size_t)d->tokens * (d->head_dim / 2) * sizeof(float2), kWsAlign);
-}
-
-int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, const float* w_scale,
-                   const int32_t* pos, const float* gq, const float* gk, void* q_out, void* k_out,
-                   void* v_out, void* workspace, size_t ws_bytes, void* stream) {
-  int rc = qkv_check(d);
-  if (rc != MRA_OK) return rc;
-  if (d->tokens == 0) return MRA_OK;
-  if (!x || !w8 || !w_scale || !pos || !gq || !gk || !q_out || !k_out || !v_out) return MRA_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w8, 16) || !aligned(w_scale, 16) || !aligned(gq, 16) ||
-      !aligned(gk, 16) || !aligned(pos, 4) || !aligned(q_out, 16) || !aligned(k_out, 16) ||
-      !aligned(v_out, 16))
-    return MRA_ERR_STRIDE;
-  const size_t need = mrope_qkv_proj_workspace_size(d);
-  if (!workspace || ws_bytes < need || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
-  const char* fi = std::getenv("MRA_FAULT_INJECT");
-  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
-
-  // the rotary table of the tokens, from the same kernel the attention uses
-  Args a;
-  std::memset(&a, 0, sizeof(a));
-  a.pos = pos;
-  a.B = 1;
-  a.S = d->tokens;
-  a.cs = (float2*)workspace;
-  const int half = d->head_dim / 2;
-  for (int j = 0; j < half; ++j)
-    a.rope.inv_freq[j] = (float)std::pow((double)d->theta, -2.0 * j / d->head_dim);
-  a.rope.sec_t = d->section[0];
-  a.rope.sec_th = d->section[0] + d->section[1];
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t n = (int64_t)d->tokens * half;
-  hipLaunchKernelGGL(mra::rope_table_kernel<128>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
-
-  mra::QkvArgs g;
-  std::memset(&g, 0, sizeof(g));
-  g.x = (const uint16_t*)x;
-  g.xs = d->x_stride;
-  g.w8 = w8;
-  g.wsc = w_scale;
-  g.cs = (const float2*)workspace;
-  g.gq = gq;
-  g.gk = gk;
-  g.gqs = d->gamma_per_head ? d->head_dim : 0;
-  g.inter = d->rope_pairs == MRA_ROPE_INTERLEAVED;
-  g.out[0] = (uint16_t*)q_out; g.out[1] = (uint16_t*)k_out; g.out[2] = (uint16_t*)v_out;
-  const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
-  for (int i = 0; i < 3; ++i) { g.os[i][0] = st[i][0]; g.os[i][1] = st[i][1]; }
-  g.M = d->tokens;
-  g.hidden = d->hidden;
-  g.H = d->heads;
-  g.n_mt = (d->tokens + 255) / 256;
-  g.eps = d->eps;
-  const float scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
-  g.qscale = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL(mra::qkv_proj_kernel<128>, dim3((unsigned)(g.n_mt * 3 * d->heads)), dim3(256), 0, s, g);
-  return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
-}
-
 }  // extern "C"
+
+// the backward and projection entry points share the helpers above
+#include "bwd_host.hpp"
+#include "qkv_host.hpp"
