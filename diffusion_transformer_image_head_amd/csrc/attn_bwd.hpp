@@ -210,13 +210,17 @@ __device__ __forceinline__ void dgamma_partial(float (&dg)[D / 32][16], float* r
 }
 
 // dK and dV: one workgroup per (batch, head, 128 keys), 32 keys per wave;
-// query tiles of 32 stream through double-buffered LDS. INTER: interleaved
-// rotary pairs (2j, 2j + 1) in the epilogue's inverse rotation.
-template <int D, bool INTER>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
+// query tiles of 32 stream through LDS. INTER: interleaved rotary pairs
+// (2j, 2j + 1) in the epilogue's inverse rotation. MODE 0 computes both (one
+// wave per SIMD: dK, dV and K' take most of the registers; four stages);
+// MODE 1 only dV (S, P, dV) and MODE 2 only dK (S, P, dP, dS, dK): each of
+// those recomputes S but fits two waves per SIMD (two stages).
+template <int D, bool INTER, int MODE>
+__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs g) {
   constexpr int KC = D / 16, DB = D / 32, BQ = 32, TILEB = BQ * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
-  constexpr int NST = 4;             // pipeline stages: NST - 1 query tiles in flight
+  constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
+  constexpr int NST = MODE == 0 ? 4 : 2;  // pipeline stages: NST - 1 query tiles in flight
   constexpr int LOADS = 2 * RUNS + 1;  // direct loads per wave per tile
   static_assert(D == 128, "the backward kernels are written for head_dim 128");
   // Stage p holds Q'' (Qp), dO (Op) and the (l2, D) pairs (Lp) of one query
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   __shared__ __attribute__((aligned(256))) float L3[2 * BQ];
   // V rows of the workgroup's 128 keys (row = key, chunk c at c ^ (row & 15)):
   // read back as B operands each tile instead of held in registers
-  __shared__ __attribute__((aligned(1024))) char Vk[128 * D * 2];
+  __shared__ __attribute__((aligned(1024))) char Vk[DO_DK ? 128 * D * 2 : 16];
   __shared__ float red[4 * D];
   auto qb = [&](auto par) -> char* {
     constexpr int p = decltype(par)::value;
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
       const u32x4 wv = *(const u32x4*)(vr + c * 16 + hf * 8);
       const u32x4 z = {0u, 0u, 0u, 0u};
       kf[c] = __builtin_bit_cast(bf16x8, kvalid ? wk : z);
-      *(u32x4*)(vrow + (((2 * c + hf) ^ (m & 15)) << 4)) = kvalid ? wv : z;
+      if constexpr (DO_DK) *(u32x4*)(vrow + (((2 * c + hf) ^ (m & 15)) << 4)) = kvalid ? wv : z;
     }
   }
 
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
-  static_assert(2 * LOADS < 16 && NST - 2 == 2, "vmcnt immediates below");
+  static_assert(2 * LOADS < 16 && (NST == 2 || NST == 4), "vmcnt immediates and the step unroll below");
 
   const int nq = (S + BQ - 1) / BQ;
   auto skipped = [&](int qt) { const int n0 = qt * BQ; return n0 >= L && min(n0 + BQ, S) <= T; };
@@ -350,10 +354,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
   int last = qt, ahead = 0;  // last tile issued; tiles issued after qt
   if (qt < nq) {
     issue(qt, Parity<0>{});
-    int t1 = next_q(qt);
-    if (t1 < nq) { issue(t1, Parity<1>{}); last = t1; ++ahead; }
-    int t2 = t1 < nq ? next_q(t1) : nq;
-    if (t2 < nq) { issue(t2, Parity<2>{}); last = t2; ++ahead; }
+    if constexpr (NST == 4) {
+      int t1 = next_q(qt);
+      if (t1 < nq) { issue(t1, Parity<1>{}); last = t1; ++ahead; }
+      int t2 = t1 < nq ? next_q(t1) : nq;
+      if (t2 < nq) { issue(t2, Parity<2>{}); last = t2; ++ahead; }
+    }
   }
 
   // tile qt sits in stage `parity`; the tile issued here goes to the stage
@@ -385,6 +391,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
       pf[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(sacc[i] - ldv[i >> 1][(i & 1) * 2]);
     __builtin_amdgcn_sched_barrier(0);
     // dV^T += dO^T P
+    if constexpr (DO_DV) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -399,6 +406,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
         dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[u], dvacc[db], 0, 0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (DO_DK) {
     // dP (queries x keys) = dO V^T
     f32x16 dpacc = {};
 #pragma unroll
@@ -426,6 +435,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
         const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
         dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, dsf[u], dkacc[db], 0, 0, 0);
       }
+    }
     qt = next_q(qt);
     --ahead;
   };
@@ -433,14 +443,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
     step(Parity<0>{});
     if (qt >= nq) break;
     step(Parity<1>{});
-    if (qt >= nq) break;
-    step(Parity<2>{});
-    if (qt >= nq) break;
-    step(Parity<3>{});
+    if constexpr (NST == 4) {
+      if (qt >= nq) break;
+      step(Parity<2>{});
+      if (qt >= nq) break;
+      step(Parity<3>{});
+    }
   }
 
   // dV rows: dims db*32 + (i/4)*8 + hf*4 + i%4 of key `key`
-  if (kin) {
+  if (DO_DV && kin) {
     uint16_t* dvp = (uint16_t*)g.dv + b * a.vs0 + (int64_t)key * a.vs1 + head * a.vs2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -451,6 +463,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs g) {
         *(u32x2*)(dvp + db * 32 + gq * 8 + hf * 4) = u32x2{w0, w1};
       }
   }
+  if constexpr (!DO_DK) return;
   // dK' = ln2 * Q''-accumulator, then the transpose rotation and RMSNorm backward
   float dg[DB][16];
   {

@@ -87,11 +87,25 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, aq);
   const int64_t rows = tokens * d->heads;
   hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
+  // dK and dV: one fused kernel, or (MRA_BWD_SPLIT) two that each recompute S
+#ifndef MRA_BWD_SPLIT
+#define MRA_BWD_SPLIT 1
+#endif
   if (g.a.inter) {
-    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    if (MRA_BWD_SPLIT) {
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 1>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 2>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    } else {
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 0>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    }
     hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
   } else {
-    hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    if (MRA_BWD_SPLIT) {
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 1>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 2>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    } else {
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 0>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    }
     hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
   }
   if (dgamma_q || dgamma_k) {
