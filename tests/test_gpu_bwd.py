@@ -148,3 +148,32 @@ def test_bwd_ragged_items():
     ref = oracle_bwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens, do,
                      text_pad=w.text_pad, section=w.section)
     check_bwd(got, ref, "ragged 4x448")
+
+
+def test_bwd_fused_qkv_views():
+    """q, k, v as strided views of one [B, S, 3, H, D] projection output, and
+    dq, dk, dv written into the matching views of one gradient buffer (the
+    layout a fused qkv projection's backward consumes): equal to the
+    contiguous call, bit for bit."""
+    import torch
+    from diffusion_transformer_image_head_amd.binding import mrope_attn, mrope_attn_bwd
+    say("case: bwd on fused qkv views")
+    w = make_workload(**SMALL["ragged157"], dtype="bf16", seed=740)
+    dev = to_dev(w)
+    do = torch.from_numpy(dout_for(w)).cuda().to(torch.bfloat16)
+    kw = dict(text_pad=w.text_pad, section=w.section)
+    qkv = torch.stack([dev["q"], dev["k"], dev["v"]], dim=2)            # [B, S, 3, H, D]
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    out, lse = mrope_attn(q, k, v, dev["pos"], dev["gamma_q"], dev["gamma_k"], dev["seq_lens"],
+                          return_lse=True, **kw)
+    grad = torch.full_like(qkv, float("nan"))
+    g1 = mrope_attn_bwd(q, k, v, dev["pos"], dev["gamma_q"], dev["gamma_k"], dev["seq_lens"], out,
+                        lse, do, dq=grad[:, :, 0], dk=grad[:, :, 1], dv=grad[:, :, 2], **kw)
+    out2, lse2 = mrope_attn(dev["q"], dev["k"], dev["v"], dev["pos"], dev["gamma_q"], dev["gamma_k"],
+                            dev["seq_lens"], return_lse=True, **kw)
+    g2 = mrope_attn_bwd(dev["q"], dev["k"], dev["v"], dev["pos"], dev["gamma_q"], dev["gamma_k"],
+                        dev["seq_lens"], out2, lse2, do, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    for a, b in zip((grad[:, :, 0], grad[:, :, 1], grad[:, :, 2], g1[3], g1[4]), (g2[0], g2[1], g2[2], g2[3], g2[4])):
+        assert torch.equal(a, b)
