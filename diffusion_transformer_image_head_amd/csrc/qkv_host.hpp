@@ -83,11 +83,15 @@ int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, cons
   g.M = d->tokens;
   g.hidden = d->hidden;
   g.H = d->heads;
-  g.n_mt = (d->tokens + 255) / 256;
   g.eps = d->eps;
   const float scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   g.qscale = (float)((double)scale * 1.4426950408889634);
-  hipLaunchKernelGGL(mra::qkv_proj_kernel<128>, dim3((unsigned)(g.n_mt * 3 * d->heads)), dim3(256), 0, s, g);
+  // one workgroup per (token tile, head pair); two workgroups share a CU
+  constexpr int kWaves = MRA_QKV_WAVES, kTok = MRA_QKV_TPW * (MRA_QKV_WAVES / 2);
+  const int head_pairs = (3 * d->heads + 1) / 2;
+  g.n_mt = (d->tokens + kTok - 1) / kTok;
+  hipLaunchKernelGGL((mra::qkv_proj_kernel<128, kWaves, MRA_QKV_KB, MRA_QKV_NST, MRA_QKV_TPW>),
+                     dim3((unsigned)(g.n_mt * head_pairs)), dim3(64 * kWaves), 0, s, g);
   return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
 }
 

@@ -85,11 +85,24 @@ def test_qkv_1024px_sampled_rows():
     say("case: qkv 1024px sampled rows")
     w = make_qkv_workload(1, 32, 128, (16, 24, 24), 512, 64, 64, 4096, seed=810)
     _, got = run_proj(w)
-    rows = np.array(sorted({0, 1, 255, 256, 511, 512, 4095, 4606, 4607} |
+    rows = np.array(sorted({0, 1, 255, 256, 511, 512, 4095, 4096, 4159, 4160, 4606, 4607} |
                            set(np.random.default_rng(0).choice(4608, 40, replace=False).tolist())))
     ref = oracle_qkv_proj(w.x, w.w8, w.w_scale, w.pos, w.gamma_q, w.gamma_k, heads=32, head_dim=128,
                           section=w.section, qscale=qscale(), rows=rows)
     check_proj([g[rows] for g in got], ref, "1024px rows")
+
+
+def test_qkv_more_than_one_round():
+    """32 heads (48 head pairs), 1380 tokens: 11 token tiles of 128 (the last
+    ragged, 100 tokens) make 528 workgroups, past one round of the 512
+    resident slots. Every element is checked."""
+    say("case: qkv more than one round of workgroups (1380 tokens, 32 heads)")
+    w = make_qkv_workload(1, 32, 128, (16, 24, 24), 8, 28, 49, 256, seed=840)
+    assert w.x.shape[0] == 1380
+    _, got = run_proj(w)
+    ref = oracle_qkv_proj(w.x, w.w8, w.w_scale, w.pos, w.gamma_q, w.gamma_k, heads=32, head_dim=128,
+                          section=w.section, qscale=qscale())
+    check_proj(got, ref, "1380 tokens")
 
 
 def test_projection_then_attention_end_to_end():
