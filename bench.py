@@ -288,6 +288,75 @@ def bench_bwd(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_packed(args):
+    """A configuration's prompts packed back to back (cu_seqlens; each
+    prompt's true-length text tokens then its image) instead of padded:
+    `steps` calls of the packed forward (prologue + attention), or with
+    --backward of the packed backward after one untimed forward. FLOPs are the
+    sequences' own: 4 H D sum(n_b^2), times 2.5 for the backward."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn_bwd_varlen, mrope_attn_varlen
+    from diffusion_transformer_image_head_amd.workloads import CONFIGS, make_varlen_workload, round_to_bf16
+
+    lib()
+    c = CONFIGS[args.config]
+    lens = c["text_lens"] if c["text_lens"] is not None else (c["text_pad"],) * c["batch"]
+    w = make_varlen_workload(c["heads"], c["head_dim"], c["section"], text_lens=lens,
+                             grids=[(c["grid_h"], c["grid_w"])] * c["batch"], sigma=c["sigma"],
+                             seed=c["seed"])
+    dev = torch.device("cuda:0")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    q, k, v = (t(x).to(torch.bfloat16) for x in (w.q, w.k, w.v))
+    pos, gq, gk = t(w.pos), t(w.gamma_q), t(w.gamma_k)
+    cu = t(w.cu_seqlens.astype(np.int32))
+    ms_len = w.max_seqlen
+    out = torch.empty_like(q)
+    ws = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    _, lse = mrope_attn_varlen(q, k, v, pos, gq, gk, cu, ms_len, section=w.section, return_lse=True,
+                               out=out, workspace=ws)
+    if args.backward:
+        do = t(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32)))
+        do = do.to(torch.bfloat16)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+        def step():
+            mrope_attn_bwd_varlen(q, k, v, pos, gq, gk, cu, ms_len, out, lse, do, section=w.section,
+                                  dq=dq, dk=dk, dv=dv, workspace=ws)
+    else:
+        def step():
+            mrope_attn_varlen(q, k, v, pos, gq, gk, cu, ms_len, section=w.section, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    mult = 2.5 if args.backward else 1.0
+    value = mult * w.flops() / (ms * 1e-3) / 1e12
+    what = "backward" if args.backward else "forward"
+    rec = {
+        "metric": f"fused QK-norm+M-RoPE attention {what} TFLOP/s, packed sequences"
+                  + (" (2.5x forward FLOPs)" if args.backward else ""),
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/dO, U[0.5,1.5) gammas; no dataset or weights)",
+        "config": {"workload": f"{args.config} packed {what}: {len(lens)} sequences, "
+                               f"{w.q.shape[0]} tokens, H={c['heads']} head_dim={c['head_dim']}",
+                   "cu_seqlens": [int(x) for x in w.cu_seqlens]},
+        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": f"whole packed {what} call"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +373,9 @@ def main():
                          "attention on its operands (kprologue none)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (dq, dk, dv, dgammas) instead of the forward")
+    ap.add_argument("--packed", action="store_true",
+                    help="pack the configuration's prompts back to back (cu_seqlens) and time the "
+                         "packed forward, or with --backward the packed backward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -317,6 +389,9 @@ def main():
 
     if args.config == "cfg1024":
         bench_cfg(args)
+        return
+    if args.packed:
+        bench_packed(args)
         return
     if args.backward:
         bench_bwd(args)

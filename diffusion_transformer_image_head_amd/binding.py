@@ -116,6 +116,12 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp, f32p,
                                      vp, vp, vp, vp, f32p, f32p, vp, ctypes.c_size_t, vp]
         L.mrope_attn_bwd.restype = ctypes.c_int
+        L.mrope_attn_bwd_varlen_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32]
+        L.mrope_attn_bwd_varlen_workspace_size.restype = ctypes.c_size_t
+        L.mrope_attn_bwd_varlen.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p,
+                                            ctypes.c_int32, vp, f32p, vp, vp, vp, vp, f32p, f32p, vp,
+                                            ctypes.c_size_t, vp]
+        L.mrope_attn_bwd_varlen.restype = ctypes.c_int
         L.mrope_qkv_proj_workspace_size.argtypes = [ctypes.POINTER(QkvDesc)]
         L.mrope_qkv_proj_workspace_size.restype = ctypes.c_size_t
         L.mrope_qkv_proj.argtypes = [ctypes.POINTER(QkvDesc), vp, vp, f32p, i32p, f32p, f32p, vp, vp, vp,
@@ -398,6 +404,53 @@ def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, 
                               lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                               dv.data_ptr(), dgq.data_ptr(), dgk.data_ptr(),
                               None if not need else workspace.data_ptr(), need, stream)
+    if rc != 0:
+        raise MraError(rc, status_string(rc))
+    return dq, dk, dv, dgq, dgk
+
+
+def mrope_attn_bwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: int, out, lse,
+                          dout, *, section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
+                          scale=None, dq=None, dk=None, dv=None, workspace=None,
+                          rope_pairs="half"):
+    """Backward of :func:`mrope_attn_varlen` (bf16, head_dim 128): q, k, v,
+    out, dout [T, H, D], pos [T, 3], cu_seqlens [B + 1] int32 on the GPU, lse
+    the forward's [H, T]. Returns (dq, dk, dv, dgamma_q, dgamma_k); rows of
+    tokens outside every sequence are left as they were in dq, dk, dv."""
+    import torch
+
+    if q.dim() != 3 or pos.dim() != 2:
+        raise ValueError("q, k, v must be [T, H, D] and pos [T, 3] for the packed form")
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a GPU int32 [B + 1] tensor")
+    cu_seqlens = cu_seqlens.contiguous()
+    t, h, d = q.shape
+    desc, _, _, _ = _checked(q[None], k[None], v[None], pos[None], gamma_q, gamma_k, None, out[None],
+                             False, text_pad=0, section=section, theta=theta, eps=eps, scale=scale,
+                             kprologue="auto", rope_pairs=rope_pairs)
+    desc.batch = cu_seqlens.numel() - 1
+    if tuple(dout.shape) != tuple(q.shape) or _bsd_strides(dout[None]) != _bsd_strides(out[None]):
+        raise ValueError("dout must have out's shape and strides")
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (h, t) or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous float32 [H, T] log-sum-exp")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, tt, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if tt.shape != ref.shape or _bsd_strides(tt[None]) != _bsd_strides(ref[None]):
+            raise ValueError(f"{name} must have the strides of its input")
+    dgq = torch.empty(gamma_q.shape, dtype=torch.float32, device=q.device)
+    dgk = torch.empty(gamma_k.shape, dtype=torch.float32, device=q.device)
+    need = int(lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(desc), int(max_seqlen)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mrope_attn_bwd_varlen(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     pos.data_ptr(), gamma_q.data_ptr(), gamma_k.data_ptr(),
+                                     cu_seqlens.data_ptr(), int(max_seqlen), out.data_ptr(),
+                                     lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                     dv.data_ptr(), dgq.data_ptr(), dgk.data_ptr(),
+                                     None if not need else workspace.data_ptr(), need, stream)
     if rc != 0:
         raise MraError(rc, status_string(rc))
     return dq, dk, dv, dgq, dgk

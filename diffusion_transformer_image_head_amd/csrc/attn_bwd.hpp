@@ -259,20 +259,26 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = tile % g.n_t, bh = tile / g.n_t;
   const int head = bh % a.H, b = bh / a.H;
-  const int S = a.S, T = a.T;
+  // item b: S tokens from token tok0 of slice bl (packed sequences: one
+  // slice of Ss tokens); token indices below are the item's own
+  const SeqView sv = seq_view(a, b);
+  const int S = sv.S, T = a.T, Ss = a.S, bl = sv.bl;
+  const int64_t tok0 = sv.tok0;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
   auto tok_ok = [&](int n) { return n < S && !(n >= L && n < T); };
   const int key = kt * 128 + wave * 32 + m;
   const bool kvalid = tok_ok(key), kin = key < S;
-  const int kc = min(key, S - 1);
+  // slice row of this lane's key, clamped into the slice (keys past the
+  // item's end read some row of it and are then zeroed or not written)
+  const int64_t kg = min(tok0 + max(min(key, S - 1), 0), (int64_t)Ss - 1);
 
   // this lane's key row of K' as B operands (dims c*16 + hf*8 + e); its V
   // row goes to LDS in the same chunk order
   bf16x8 kf[KC];
   char* vrow = Vk + (wave * 32 + m) * (D * 2);
   {
-    const uint16_t* kr = a.kp + (((int64_t)b * a.H + head) * S + kc) * D;
-    const uint16_t* vr = (const uint16_t*)a.v + b * a.vs0 + (int64_t)kc * a.vs1 + head * a.vs2;
+    const uint16_t* kr = a.kp + (((int64_t)bl * a.H + head) * Ss + kg) * D;
+    const uint16_t* vr = (const uint16_t*)a.v + bl * a.vs0 + kg * a.vs1 + head * a.vs2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 wk = *(const u32x4*)(kr + c * 16 + hf * 8);
@@ -286,13 +292,14 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
   // streamed tiles: run j of this wave fills LDS bytes [(wave*RUNS+j)*1024,
   // +1024) = rows 4*(wave*RUNS+j) + L/16, physical chunk L%16; every wave also
   // loads the tile's 32 (l2, D) pairs (lane L: float L), the same 256 bytes
-  const uint16_t* qbase = g.qp + ((int64_t)b * a.H + head) * S * D;
+  // every stream covers the item's S rows only: rows past them read zeros
+  const uint16_t* qbase = g.qp + (((int64_t)bl * a.H + head) * Ss + tok0) * D;
   const uint32_t qnrec = (uint32_t)((int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qbase, qnrec);
-  const uint16_t* obase = (const uint16_t*)g.dout + b * g.ds0 + head * g.ds2;
-  const uint32_t onrec = (uint32_t)(((int64_t)(S - 1) * g.ds1 + D) * 2);
+  const uint16_t* obase = (const uint16_t*)g.dout + bl * g.ds0 + tok0 * g.ds1 + head * g.ds2;
+  const uint32_t onrec = S > 0 ? (uint32_t)(((int64_t)(S - 1) * g.ds1 + D) * 2) : 0u;
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(obase, onrec);
-  const float* ldbase = g.ld + ((int64_t)b * a.H + head) * S * 2;
+  const float* ldbase = g.ld + (((int64_t)bl * a.H + head) * Ss + tok0) * 2;
   const uint32_t lnrec = (uint32_t)((int64_t)S * 2 * 4);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(ldbase, lnrec);
   int t_item[RUNS], q_src[RUNS], o_src[RUNS];
@@ -343,10 +350,10 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
   const int t_key0 = (vg >> 1) * 16 + (vj >> 2);
   const int t_dim0 = 16 * (vg & 1) + 4 * (vj & 3);
 
-  // a workgroup whose 128 keys are all padding (or past the end) has zero
-  // dk and dv
+  // a workgroup whose 128 keys are all padding or past the item's end has
+  // zero dk and dv
   const int k0 = kt * 128;
-  const bool all_pad = k0 >= L && min(k0 + 128, S) <= T;
+  const bool all_pad = (k0 >= L && min(k0 + 128, S) <= T) || k0 >= S;
   int qt = 0;
   while (qt < nq && skipped(qt)) ++qt;
   if (all_pad) qt = nq;
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
 
   // dV rows: dims db*32 + (i/4)*8 + hf*4 + i%4 of key `key`
   if (DO_DV && kin) {
-    uint16_t* dvp = (uint16_t*)g.dv + b * a.vs0 + (int64_t)key * a.vs1 + head * a.vs2;
+    uint16_t* dvp = (uint16_t*)g.dv + bl * a.vs0 + (tok0 + key) * a.vs1 + head * a.vs2;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -467,9 +474,9 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
   // dK' = ln2 * Q''-accumulator, then the transpose rotation and RMSNorm backward
   float dg[DB][16];
   {
-    const uint16_t* xrow = (const uint16_t*)a.k + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
-    const float2* csrow = a.cs + ((int64_t)b * S + kc) * (D / 2);
-    uint16_t* dst = (uint16_t*)g.dk + b * a.ks0 + (int64_t)kc * a.ks1 + head * a.ks2;
+    const uint16_t* xrow = (const uint16_t*)a.k + bl * a.ks0 + kg * a.ks1 + head * a.ks2;
+    const float2* csrow = a.cs + ((int64_t)bl * Ss + kg) * (D / 2);
+    uint16_t* dst = (uint16_t*)g.dk + bl * a.ks0 + kg * a.ks1 + head * a.ks2;
     rope_rms_bwd<D, INTER>(dkacc, kLn2, xrow, a.gk + head * a.gqs, csrow, a.eps, kvalid, kin, dst,
                            hf, dg);
   }
@@ -494,18 +501,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int qtile = tile % g.n_t, bh = tile / g.n_t;
   const int head = bh % a.H, b = bh / a.H;
-  const int S = a.S, T = a.T;
+  // item b: S tokens from token tok0 of slice bl, as in the dK/dV kernel
+  const SeqView sv = seq_view(a, b);
+  const int S = sv.S, T = a.T, Ss = a.S, bl = sv.bl;
+  const int64_t tok0 = sv.tok0;
   const int L = a.seq_lens ? min(max(a.seq_lens[b], 0), T) : T;
   auto tok_ok = [&](int n) { return n < S && !(n >= L && n < T); };
   const int qrow = qtile * 128 + wave * 32 + m;
   const bool qvalid = tok_ok(qrow), qin = qrow < S;
-  const int qc = min(qrow, S - 1);
+  const int64_t qg = min(tok0 + max(min(qrow, S - 1), 0), (int64_t)Ss - 1);
 
   // this lane's query row of Q'' and dO as B operands
   bf16x8 qf[KC], dof[KC];
   {
-    const uint16_t* qr = g.qp + (((int64_t)b * a.H + head) * S + qc) * D;
-    const uint16_t* dr = (const uint16_t*)g.dout + b * g.ds0 + (int64_t)qc * g.ds1 + head * g.ds2;
+    const uint16_t* qr = g.qp + (((int64_t)bl * a.H + head) * Ss + qg) * D;
+    const uint16_t* dr = (const uint16_t*)g.dout + bl * g.ds0 + qg * g.ds1 + head * g.ds2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const u32x4 wq = *(const u32x4*)(qr + c * 16 + hf * 8);
@@ -515,15 +525,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
       dof[c] = __builtin_bit_cast(bf16x8, qvalid ? wd : z);
     }
   }
-  const int64_t rowi = ((int64_t)b * a.H + head) * S + qc;
+  const int64_t rowi = ((int64_t)bl * a.H + head) * Ss + qg;
   const float l2v = qvalid ? g.ld[2 * rowi] : INFINITY;
   const float dl = qvalid ? g.ld[2 * rowi + 1] : 0.f;
 
-  const uint16_t* kbase = a.kp + ((int64_t)b * a.H + head) * S * D;
+  const uint16_t* kbase = a.kp + (((int64_t)bl * a.H + head) * Ss + tok0) * D;
   const uint32_t knrec = (uint32_t)((int64_t)S * D * 2);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, knrec);
-  const uint16_t* vbase = (const uint16_t*)a.v + b * a.vs0 + head * a.vs2;
-  const uint32_t vnrec = (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2);
+  const uint16_t* vbase = (const uint16_t*)a.v + bl * a.vs0 + tok0 * a.vs1 + head * a.vs2;
+  const uint32_t vnrec = S > 0 ? (uint32_t)(((int64_t)(S - 1) * a.vs1 + D) * 2) : 0u;
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, vnrec);
   int t_item[RUNS], k_src[RUNS], v_src[RUNS];
 #pragma unroll
@@ -563,9 +573,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
   const int t_key0 = (vg >> 1) * 16 + (vj >> 2);
   const int t_dim0 = 16 * (vg & 1) + 4 * (vj & 3);
 
-  // a workgroup whose 128 queries are all padding computes nothing
+  // a workgroup whose 128 queries are all padding or past the item's end
+  // computes nothing
   const int q0 = qtile * 128;
-  const bool all_pad = q0 >= L && min(q0 + 128, S) <= T;
+  const bool all_pad = (q0 >= L && min(q0 + 128, S) <= T) || q0 >= S;
   int kt = 0;
   while (kt < nk && skipped(kt)) ++kt;
   if (all_pad) kt = nk;
@@ -624,9 +635,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
 
   float dg[DB][16];
   {
-    const uint16_t* xrow = (const uint16_t*)a.q + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
-    const float2* csrow = a.cs + ((int64_t)b * S + qc) * (D / 2);
-    uint16_t* dst = (uint16_t*)g.dq + b * a.qs0 + (int64_t)qc * a.qs1 + head * a.qs2;
+    const uint16_t* xrow = (const uint16_t*)a.q + bl * a.qs0 + qg * a.qs1 + head * a.qs2;
+    const float2* csrow = a.cs + ((int64_t)bl * Ss + qg) * (D / 2);
+    uint16_t* dst = (uint16_t*)g.dq + bl * a.qs0 + qg * a.qs1 + head * a.qs2;
     rope_rms_bwd<D, INTER>(dqacc, a.scale, xrow, a.gq + head * a.gqs, csrow, a.eps, qvalid, qin, dst,
                            hf, dg);
   }

@@ -1,6 +1,7 @@
-// Host side of the backward entry points (mrope_attn_bwd and its workspace
-// query). Included once, at the end of mrope_attn.hip, whose helpers it uses;
-// kept in its own file so the forward path's sources stand alone.
+// Host side of the backward entry points (mrope_attn_bwd, its packed
+// variable-length form mrope_attn_bwd_varlen, and their workspace queries).
+// Included once, at the end of mrope_attn.hip, whose helpers it uses; kept in
+// its own file so the forward path's sources stand alone.
 #pragma once
 
 extern "C" {
@@ -8,17 +9,19 @@ extern "C" {
 // ---- backward pass ---------------------------------------------------------
 // Workspace: (cos, sin) table [B, S, D/2] float2, K' and Q'' [B, H, S, D] bf16,
 // (l2, D) pairs [B, H, S, 2] fp32, then the gamma partials of the dq and dk/dv
-// workgroups [n_wg, D] fp32 each; every piece 256-byte aligned.
+// workgroups [n_wg, D] fp32 each; every piece 256-byte aligned. B and S are
+// the tensor layout's (one slice of every token for packed sequences); the
+// workgroups cover nseq items of at most maxlen tokens, 128 per tile.
 struct BwdPlan {
   int n_t, n_wg;
   size_t off_cs, off_kp, off_qp, off_ld, off_gq, off_gk, bytes;
 };
 
-static BwdPlan bwd_plan(const mra_desc* d) {
+static BwdPlan bwd_plan(const mra_desc* d, int nseq, int maxlen) {
   BwdPlan p;
   const size_t rows = (size_t)d->batch * d->seq * d->heads;
-  p.n_t = (d->seq + 127) / 128;
-  p.n_wg = d->batch * d->heads * p.n_t;
+  p.n_t = (maxlen + 127) / 128;
+  p.n_wg = nseq * d->heads * p.n_t;
   size_t off = 0;
   p.off_cs = off; off += table_bytes(d);
   p.off_kp = off; off += round_up(rows * d->head_dim * 2, kWsAlign);
@@ -38,29 +41,23 @@ static int bwd_check(const mra_desc* d) {
   return MRA_OK;
 }
 
-size_t mrope_attn_bwd_workspace_size(const mra_desc* d) {
-  if (bwd_check(d) != MRA_OK || d->batch == 0 || d->seq == 0) return 0;
-  return bwd_plan(d).bytes;
+static int bwd_pointers(const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                        void* dv, const float* dgq, const float* dgk) {
+  if (!out || !lse || !dout || !dq || !dk || !dv) return MRA_ERR_NULL;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MRA_ERR_STRIDE;
+  if (!aligned(lse, 4) || !aligned(dgq, 4) || !aligned(dgk, 4)) return MRA_ERR_STRIDE;
+  return MRA_OK;
 }
 
-int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* v,
-                   const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
-                   const void* out, const float* lse, const void* dout, void* dq, void* dk,
-                   void* dv, float* dgamma_q, float* dgamma_k, void* workspace, size_t ws_bytes,
-                   void* stream) {
-  int rc = bwd_check(d);
-  if (rc != MRA_OK) return rc;
-  rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
-  if (rc != MRA_OK) return rc;
-  if (d->batch == 0 || d->seq == 0) return MRA_OK;
-  if (!lse || !dout || !dq || !dk || !dv) return MRA_ERR_NULL;
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return MRA_ERR_STRIDE;
-  if (!aligned(lse, 4) || !aligned(dgamma_q, 4) || !aligned(dgamma_k, 4)) return MRA_ERR_STRIDE;
-  const BwdPlan p = bwd_plan(d);
-  if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
-  const char* fi = std::getenv("MRA_FAULT_INJECT");
-  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
-
+// Launches the backward over layout d (validated) for nseq items of at most
+// maxlen tokens: per-item views come from seq_lens (padded layout) or
+// cu_seqlens (packed layout, d->batch == 1).
+static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_lens,
+                   const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                   const int32_t* pos, const float* gq, const float* gk, const void* out,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dgamma_q,
+                   float* dgamma_k, void* workspace, hipStream_t s) {
+  const BwdPlan p = bwd_plan(d, nseq, maxlen);
   char* w = (char*)workspace;
   mra::BwdArgs g;
   std::memset(&g, 0, sizeof(g));
@@ -77,9 +74,10 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   g.dgq = dgamma_q; g.dgk = dgamma_k;
   g.n_t = p.n_t;
 
-  hipStream_t s = (hipStream_t)stream;
+  // the row-wise passes run over the whole layout (every token of a packed
+  // slice): K' and the rotary table, then Q'' = c2 * rope(rmsnorm(q)) (same
+  // kernel), then the (l2, D) pairs
   const int64_t tokens = (int64_t)d->batch * d->seq;
-  // K' and the rotary table, then Q'' = c2 * rope(rmsnorm(q)) (same kernel)
   hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, g.a);
   Args aq = g.a;
   aq.k = q; aq.ks0 = aq.qs0; aq.ks1 = aq.qs1; aq.ks2 = aq.qs2;
@@ -87,6 +85,9 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(mra::k_prologue_kernel<128>, dim3((unsigned)((tokens + 3) / 4)), dim3(256), 0, s, aq);
   const int64_t rows = tokens * d->heads;
   hipLaunchKernelGGL(mra::bwd_delta_kernel<128>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s, g);
+  // the matrix-core kernels work per item
+  g.a.B = nseq;
+  g.a.cu_seqlens = cu_seqlens;
   // dK and dV: one fused kernel, or (MRA_BWD_SPLIT) two that each recompute S
 #ifndef MRA_BWD_SPLIT
 #define MRA_BWD_SPLIT 1
@@ -109,10 +110,10 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
     hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
   }
   if (dgamma_q || dgamma_k) {
-    // per-tile partials are laid out [B, H, n_t, D]: a shared gamma sums all
-    // of them, a per-head gamma sums head h's B * n_t rows
+    // per-tile partials are laid out [nseq, H, n_t, D]: a shared gamma sums
+    // all of them, a per-head gamma sums head h's nseq * n_t rows
     const bool ph = d->gamma_per_head;
-    const int n = ph ? d->batch * p.n_t : p.n_wg;
+    const int n = ph ? nseq * p.n_t : p.n_wg;
     const int run = ph ? p.n_t : p.n_wg;
     const int64_t stride = ph ? (int64_t)d->heads * p.n_t : 0;
     hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2u * (ph ? d->heads : 1)), dim3(8 * 128), 0, s,
@@ -120,6 +121,64 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
                        dgamma_k);
   }
   return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+}
+
+size_t mrope_attn_bwd_workspace_size(const mra_desc* d) {
+  if (bwd_check(d) != MRA_OK || d->batch == 0 || d->seq == 0) return 0;
+  return bwd_plan(d, d->batch, d->seq).bytes;
+}
+
+int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* v,
+                   const int32_t* pos, const float* gq, const float* gk, const int32_t* seq_lens,
+                   const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                   void* dv, float* dgamma_q, float* dgamma_k, void* workspace, size_t ws_bytes,
+                   void* stream) {
+  int rc = bwd_check(d);
+  if (rc != MRA_OK) return rc;
+  rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
+  if (rc != MRA_OK) return rc;
+  if (d->batch == 0 || d->seq == 0) return MRA_OK;
+  rc = bwd_pointers(out, lse, dout, dq, dk, dv, dgamma_q, dgamma_k);
+  if (rc != MRA_OK) return rc;
+  const BwdPlan p = bwd_plan(d, d->batch, d->seq);
+  if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  return bwd_run(d, d->batch, d->seq, seq_lens, nullptr, q, k, v, pos, gq, gk, out, lse, dout, dq, dk, dv,
+                 dgamma_q, dgamma_k, workspace, (hipStream_t)stream);
+}
+
+size_t mrope_attn_bwd_varlen_workspace_size(const mra_desc* d, int32_t max_seqlen) {
+  mra_desc lay;
+  if (varlen_layout(d, max_seqlen, lay) != MRA_OK || bwd_check(d) != MRA_OK) return 0;
+  if (d->batch == 0 || d->seq == 0 || max_seqlen == 0) return 0;
+  return bwd_plan(&lay, d->batch, max_seqlen).bytes;
+}
+
+int mrope_attn_bwd_varlen(const mra_desc* d, const void* q, const void* k, const void* v,
+                          const int32_t* pos, const float* gq, const float* gk,
+                          const int32_t* cu_seqlens, int32_t max_seqlen, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          float* dgamma_q, float* dgamma_k, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  mra_desc lay;
+  int rc = varlen_layout(d, max_seqlen, lay);
+  if (rc != MRA_OK) return rc;
+  rc = bwd_check(d);
+  if (rc != MRA_OK) return rc;
+  if (d->batch == 0 || d->seq == 0 || max_seqlen == 0) return MRA_OK;
+  rc = mrope_attn_validate(&lay, q, k, v, pos, gq, gk, nullptr, out);
+  if (rc != MRA_OK) return rc;
+  if (!cu_seqlens) return MRA_ERR_NULL;
+  if (!aligned(cu_seqlens, 4)) return MRA_ERR_STRIDE;
+  rc = bwd_pointers(out, lse, dout, dq, dk, dv, dgamma_q, dgamma_k);
+  if (rc != MRA_OK) return rc;
+  const BwdPlan p = bwd_plan(&lay, d->batch, max_seqlen);
+  if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
+  const char* fi = std::getenv("MRA_FAULT_INJECT");
+  if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  return bwd_run(&lay, d->batch, max_seqlen, nullptr, cu_seqlens, q, k, v, pos, gq, gk, out, lse, dout, dq,
+                 dk, dv, dgamma_q, dgamma_k, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

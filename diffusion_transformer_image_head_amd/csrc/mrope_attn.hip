@@ -254,7 +254,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 105; }
+int mrope_attn_abi_version(void) { return 106; }
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {

@@ -230,7 +230,7 @@ int mrope_attn_fwd_varlen(const mra_desc* desc, const void* q, const void* k, co
  * head_dim 128 only (else MRA_ERR_UNSUPPORTED). dout has out's strides
  * (o_stride); dq, dk, dv have q's, k's and v's strides; all four must be
  * 16-byte aligned and must not overlap the inputs or each other. The packed
- * (cu_seqlens) layout has no backward here. */
+ * (cu_seqlens) layout's backward is mrope_attn_bwd_varlen below. */
 size_t mrope_attn_bwd_workspace_size(const mra_desc* desc);
 
 int mrope_attn_bwd(const mra_desc* desc, const void* q, const void* k, const void* v,
@@ -238,6 +238,22 @@ int mrope_attn_bwd(const mra_desc* desc, const void* q, const void* k, const voi
                    const int32_t* seq_lens, const void* out, const float* lse, const void* dout,
                    void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of mrope_attn_fwd_varlen (packed variable-length sequences; the
+ * layout, cu_seqlens, max_seqlen and lse [H, seq] as described there): the
+ * same gradients as mrope_attn_bwd, each sequence attending to its own
+ * tokens only; dgamma sums every sequence's rows. desc->text_pad must be 0
+ * and max_seqlen 0..seq (MRA_ERR_SHAPE); bf16 with head_dim 128 only
+ * (MRA_ERR_UNSUPPORTED). Tokens outside every sequence are not written in
+ * dq, dk, dv. batch, seq or max_seqlen 0: nothing is done. */
+size_t mrope_attn_bwd_varlen_workspace_size(const mra_desc* desc, int32_t max_seqlen);
+
+int mrope_attn_bwd_varlen(const mra_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                          const int32_t* cu_seqlens, int32_t max_seqlen, const void* out,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          float* dgamma_q, float* dgamma_k, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* ---- fp8 QKV projection with the norm/rotation epilogue ------------------
  *

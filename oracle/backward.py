@@ -110,3 +110,38 @@ def oracle_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, dout, *, text_pad: int,
     dq, dgq = norm_bwd(q, rq, gq, dxq)
     dk, dgk = norm_bwd(k, rk, gk, dxk)
     return dq, dk, dv, dgq, dgk
+
+
+def oracle_bwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, dout, *, section=(16, 24, 24),
+                      theta: float = 10000.0, eps: float = 1e-6, scale=None,
+                      rope_pairs: str = "half"):
+    """Gradients of sum(dout * out) for the packed form
+    (``oracle.reference.oracle_fwd_varlen``): sequence b is tokens
+    [cu_seqlens[b], cu_seqlens[b+1]) of q, k, v, dout [T, H, D] and pos
+    [T, 3]. Each sequence is an independent padding-free problem, so its
+    gradients are :func:`oracle_bwd` of that sequence alone; a gamma is
+    shared by every sequence, so its gradient is the sum over them.
+
+    Returns (dq, dk, dv [T, H, D], dgamma_q, dgamma_k) in float64; rows of
+    tokens outside every sequence are NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    t_, h_, d_ = q.shape
+    dq = np.full((t_, h_, d_), np.nan)
+    dk = np.full((t_, h_, d_), np.nan)
+    dv = np.full((t_, h_, d_), np.nan)
+    dgq = np.zeros(np.shape(gamma_q))
+    dgk = np.zeros(np.shape(gamma_k))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        a0, a1 = int(cu[b]), int(cu[b + 1])
+        if a1 <= a0:
+            continue
+        r = oracle_bwd(q[None, a0:a1], np.asarray(k)[None, a0:a1], np.asarray(v)[None, a0:a1],
+                       np.asarray(pos)[None, a0:a1], gamma_q, gamma_k, None,
+                       np.asarray(dout)[None, a0:a1], text_pad=0, section=section, theta=theta,
+                       eps=eps, scale=scale, rope_pairs=rope_pairs)
+        dq[a0:a1], dk[a0:a1], dv[a0:a1] = r[0][0], r[1][0], r[2][0]
+        dgq += r[3]
+        dgk += r[4]
+    return dq, dk, dv, dgq, dgk

@@ -39,6 +39,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_bwd",
+        "mrope_attn_bwd_varlen", "mrope_attn_bwd_varlen_workspace_size",
         "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
         "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
@@ -78,7 +79,7 @@ def test_struct_layouts_match_header(tmp_path, cls, struct):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 105
+    assert lib.mrope_attn_abi_version() == 106
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -344,6 +345,53 @@ def test_bwd_rejects_before_launch(lib, monkeypatch):
     monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
     assert _bwd(d, nbytes=need) == -8
     assert _bwd(d, nbytes=need, dg=None) == -8
+
+
+def _bwd_varlen(d, maxlen, cu=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, ws=FAKE, nbytes=1 << 40, dg=FAKE):
+    return B.lib().mrope_attn_bwd_varlen(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, cu, maxlen,
+                                         FAKE, lse, dout, dq, FAKE, FAKE, dg, dg, ws, nbytes, None)
+
+
+def test_bwd_varlen_workspace(lib):
+    # 3 packed sequences, 6000 tokens in all, the longest 2500: the row-wise
+    # pieces cover every token of the slice, the per-tile gamma partials
+    # 3 sequences x 32 heads x ceil(2500 / 128) tiles
+    d = desc(batch=3, seq=6000, heads=32, text_pad=0)
+    rows = 6000 * 32
+    n_wg = 3 * 32 * 20
+    want = 6000 * 64 * 8 + 2 * rows * 128 * 2 + 2 * rows * 4 + 2 * n_wg * 128 * 4
+    assert B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(d), 2500) == want
+    assert B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(d), 0) == 0
+    assert B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(d), 6001) == 0
+    assert B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(desc(text_pad=5)), 50) == 0
+    assert B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(desc(text_pad=0, dtype=B.MRA_FP32)),
+                                                        50) == 0
+
+
+def test_bwd_varlen_rejects_before_launch(lib, monkeypatch):
+    d = desc(text_pad=0)
+    need = B.lib().mrope_attn_bwd_varlen_workspace_size(ctypes.byref(d), 60)
+    assert need > 0
+    assert _bwd_varlen(desc(text_pad=5), 60) == -2                # text_pad must be 0
+    assert _bwd_varlen(d, 101) == -2                              # max_seqlen > seq
+    assert _bwd_varlen(d, -1) == -2
+    assert _bwd_varlen(desc(text_pad=0, head_dim=64, section=(8, 12, 12)), 60) == -6
+    assert _bwd_varlen(desc(text_pad=0, dtype=B.MRA_FP32), 60) == -6
+    assert _bwd_varlen(desc(text_pad=0, kprologue="none"), 60) == -6
+    assert _bwd_varlen(d, 60, cu=None) == -1
+    assert _bwd_varlen(d, 60, cu=FAKE + 2) == -5
+    assert _bwd_varlen(d, 60, lse=None) == -1
+    assert _bwd_varlen(d, 60, dout=None) == -1
+    assert _bwd_varlen(d, 60, dq=FAKE + 8) == -5
+    assert _bwd_varlen(d, 60, nbytes=need - 1) == -7
+    assert _bwd_varlen(d, 60, ws=None) == -7
+    # nothing to do: no sequences, no tokens, or every sequence empty
+    assert _bwd_varlen(desc(batch=0, text_pad=0), 0, cu=None, lse=None, dout=None, dq=None, ws=None,
+                       nbytes=0) == 0
+    assert _bwd_varlen(d, 0, cu=None, lse=None, dout=None, dq=None, ws=None, nbytes=0) == 0
+    monkeypatch.setenv("MRA_FAULT_INJECT", "launch")
+    assert _bwd_varlen(d, 60, nbytes=need) == -8
+    assert _bwd_varlen(d, 60, nbytes=need, dg=None) == -8
 
 
 # ---------------------------------------------------------------- operands given / fp8 QKV

@@ -177,3 +177,100 @@ def test_bwd_fused_qkv_views():
     assert torch.equal(out, out2)
     for a, b in zip((grad[:, :, 0], grad[:, :, 1], grad[:, :, 2], g1[3], g1[4]), (g2[0], g2[1], g2[2], g2[3], g2[4])):
         assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- packed sequences
+def run_bwd_varlen(w, do, max_seqlen=None, fill=None):
+    """GPU packed forward (out, lse) then GPU packed backward; float64
+    numpy results. fill: the value dq, dk, dv hold before the call."""
+    import torch
+    from diffusion_transformer_image_head_amd.binding import mrope_attn_bwd_varlen, mrope_attn_varlen
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    q, k, v = (t(x).to(torch.bfloat16) for x in (w.q, w.k, w.v))
+    pos, gq, gk = t(w.pos), t(w.gamma_q), t(w.gamma_k)
+    cu = t(np.asarray(w.cu_seqlens, dtype=np.int32))
+    ms = w.max_seqlen if max_seqlen is None else max_seqlen
+    kw = dict(section=w.section, theta=w.theta, eps=w.eps, rope_pairs=w.rope_pairs)
+    out, lse = mrope_attn_varlen(q, k, v, pos, gq, gk, cu, ms, return_lse=True, **kw)
+    bufs = {} if fill is None else {n: torch.full_like(q, fill) for n in ("dq", "dk", "dv")}
+    g = mrope_attn_bwd_varlen(q, k, v, pos, gq, gk, cu, ms, out, lse, t(do).to(torch.bfloat16), **kw,
+                              **bufs)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy().astype(np.float64) for x in g]
+
+
+def oracle_varlen(w, do):
+    from oracle.backward import oracle_bwd_varlen
+    return oracle_bwd_varlen(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.cu_seqlens, do,
+                             section=w.section, theta=w.theta, eps=w.eps, rope_pairs=w.rope_pairs)
+
+
+def inside(w):
+    cu = np.asarray(w.cu_seqlens)
+    m = np.zeros(w.q.shape[0], bool)
+    for a0, a1 in zip(cu[:-1], cu[1:]):
+        m[a0:a1] = True
+    return m
+
+
+def check_bwd_varlen(got, ref, w, what):
+    m = inside(w)
+    check_bwd([g[m] for g in got[:3]] + got[3:], [r[m] for r in ref[:3]] + list(ref[3:]), what)
+
+
+VARLEN = {
+    # lengths 134, 49, 160, 8: two 128-row tiles for the longest, so the
+    # shorter sequences' second tiles are past their ends
+    "mixed": dict(heads=3, text_lens=(17, 0, 40, 5), grids=((9, 13), (7, 7), (10, 12), (1, 3))),
+    # 493 and 84 tokens: four tiles for the first
+    "multi_tile": dict(heads=2, text_lens=(33, 64), grids=((20, 23), (4, 5))),
+}
+
+
+@pytest.mark.parametrize("name", list(VARLEN))
+def test_bwd_varlen(name):
+    from diffusion_transformer_image_head_amd.workloads import make_varlen_workload
+    c = VARLEN[name]
+    w = make_varlen_workload(c["heads"], 128, (16, 24, 24), c["text_lens"], c["grids"],
+                             seed=760 + list(VARLEN).index(name))
+    say(f"case: bwd varlen {name} cu={w.cu_seqlens.tolist()}")
+    do = dout_for(w)
+    check_bwd_varlen(run_bwd_varlen(w, do), oracle_varlen(w, do), w, f"varlen {name}")
+
+
+def test_bwd_varlen_gaps_empty_and_long_max():
+    """Tokens before, between (none) and after the sequences belong to no
+    sequence, one sequence is empty, and max_seqlen is the whole slice (many
+    tiles past every sequence's end): the sequences' gradients match the
+    oracle and the outside rows keep what dq, dk, dv held."""
+    from diffusion_transformer_image_head_amd.workloads import make_varlen_workload
+    w = make_varlen_workload(2, 128, (16, 24, 24), (9, 30), ((5, 7), (8, 8)), seed=770)
+    rng = np.random.default_rng(771)
+    t0, t1 = 5, 7                                       # tokens outside, before and after
+    grow = lambda a: np.concatenate([round_to_bf16(rng.standard_normal((t0,) + a.shape[1:]).astype(np.float32)),  # noqa: E731
+                                     a, round_to_bf16(rng.standard_normal((t1,) + a.shape[1:]).astype(np.float32))])
+    w.q, w.k, w.v = grow(w.q), grow(w.k), grow(w.v)
+    w.pos = np.concatenate([np.zeros((t0, 3), np.int32), w.pos, np.zeros((t1, 3), np.int32)])
+    cu = np.asarray(w.cu_seqlens) + t0
+    w.cu_seqlens = np.insert(cu, 1, cu[1]).astype(np.int32)    # an empty second sequence
+    say(f"case: bwd varlen gaps cu={w.cu_seqlens.tolist()} T={w.q.shape[0]}")
+    do = dout_for(w)
+    got = run_bwd_varlen(w, do, max_seqlen=w.q.shape[0], fill=7.0)
+    check_bwd_varlen(got, oracle_varlen(w, do), w, "varlen gaps")
+    out_rows = ~inside(w)
+    assert out_rows.sum() == t0 + t1
+    for g in got[:3]:
+        assert np.all(g[out_rows] == 7.0)
+
+
+@pytest.mark.parametrize("per_head,pairs", [(True, "interleaved"), (False, "interleaved"), (True, "half")])
+def test_bwd_varlen_conventions(per_head, pairs):
+    from diffusion_transformer_image_head_amd.workloads import make_varlen_workload
+    w = make_varlen_workload(3, 128, (16, 24, 24), (17, 40), ((9, 13), (6, 7)), seed=780,
+                             gamma_per_head=per_head, rope_pairs=pairs)
+    say(f"case: bwd varlen gamma_per_head={per_head} rope_pairs={pairs}")
+    do = dout_for(w)
+    got = run_bwd_varlen(w, do)
+    ref = oracle_varlen(w, do)
+    assert got[3].shape == ref[3].shape
+    check_bwd_varlen(got, ref, w, f"varlen {per_head} {pairs}")

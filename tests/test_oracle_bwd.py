@@ -103,8 +103,31 @@ def pin_bwd_shared_gamma_is_sum_over_heads():
         assert np.max(np.abs(g_head[i][0] - g_head[i][1])) > 1e-6
 
 
+def pin_bwd_varlen_is_padded_without_padding():
+    """Packing drops the padded text slots and nothing else: the packed-form
+    gradients of each sequence's tokens equal the padded-form gradients of
+    the same tokens, and the gamma gradients are equal too (padded slots
+    carry none). Checked with a shared and with a per-head gamma."""
+    for w in (_case(seed=78), _case(seed=79, gamma_per_head=True, rope_pairs="interleaved")):
+        do = np.random.default_rng(10).standard_normal(w.q.shape)
+        g_pad = _grads(w, do)
+        b_, s_ = w.q.shape[:2]
+        keep = [np.r_[0:int(l), w.text_pad:s_] for l in w.seq_lens]
+        cat = lambda a: np.concatenate([np.asarray(a)[b][keep[b]] for b in range(b_)])  # noqa: E731
+        cu = np.concatenate([[0], np.cumsum([len(kk) for kk in keep])])
+        g_pk = bwd.oracle_bwd_varlen(cat(w.q), cat(w.k), cat(w.v), cat(w.pos), w.gamma_q, w.gamma_k,
+                                     cu, cat(do), section=w.section, theta=w.theta, eps=w.eps,
+                                     rope_pairs=w.rope_pairs)
+        for i in range(3):
+            assert np.max(np.abs(g_pk[i] - cat(g_pad[i]))) < 1e-12
+        for i in (3, 4):
+            assert g_pk[i].shape == np.shape(g_pad[i])
+            assert np.max(np.abs(g_pk[i] - g_pad[i])) < 1e-12
+
+
 PINS = [pin_bwd_finite_differences, pin_bwd_padded_tokens_have_no_gradient, pin_bwd_dv_column_sum,
-        pin_bwd_position_shift_invariance, pin_bwd_shared_gamma_is_sum_over_heads]
+        pin_bwd_position_shift_invariance, pin_bwd_shared_gamma_is_sum_over_heads,
+        pin_bwd_varlen_is_padded_without_padding]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
