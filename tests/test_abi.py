@@ -173,6 +173,15 @@ def test_workspace_sizes(lib):
                                  kprologue="fused")) == 4096 * 64 * 8
     assert B.workspace_size(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
     assert B.workspace_size(desc(section=(1, 2, 3))) == 0          # invalid -> 0
+    rec = 256 * (128 // 2 + 2) * 4                                 # one part's records
+    # 36 heads: 1296 tiles leave 272 after two waves, a few more than the 256
+    # compute units: cut into 2 key ranges
+    h36 = desc(batch=1, seq=4608, heads=36, text_pad=512)
+    assert B.workspace_size(h36) == table + 4608 * 36 * 128 * 2 + 272 * 2 * rec
+    # 928 tiles leave 416: not cut; 704 tiles leave 192: not cut
+    for seq, heads in ((3712, 32), (2816, 32)):
+        d2 = desc(batch=1, seq=seq, heads=heads, text_pad=512)
+        assert B.workspace_size(d2) == seq * 64 * 8 + seq * heads * 128 * 2
     assert lib.mrope_attn_workspace_size(None) == 0
 
 
