@@ -17,7 +17,10 @@
 // workgroup per 128 keys, 32 per wave, streaming 32-query tiles of Q'' and
 // dO through LDS), bwd_dq_kernel (one workgroup per 128 queries, streaming
 // 32-key tiles of K' and V), bwd_dgamma_kernel (fixed-order sum of the
-// per-workgroup gamma partials). All matrix products use
+// per-workgroup gamma partials). The dk/dv and dq kernels work per item
+// (seq_view): a padded batch item, or one sequence of a packed layout whose
+// streams start at the sequence's first token and end with its last, so a
+// sequence only sees its own tokens. All matrix products use
 // v_mfma_f32_32x32x16_bf16 in the transposed-output form of the forward: the
 // lane's resident row (a key in dk/dv, a query in dq) is the B-operand
 // column, and the streamed tile's rows are A-operand rows read from LDS either
