@@ -17,10 +17,11 @@ namespace {
 
 using mra::Args;
 
+// Waves per attention workgroup: 0 chooses per problem (make_plan); 4 or 8
+// forces one.
 #ifndef MRA_WAVES
-#define MRA_WAVES 4
+#define MRA_WAVES 0
 #endif
-constexpr int kWaves = MRA_WAVES;
 #ifndef MRA_BLOCK_N
 #define MRA_BLOCK_N 64
 #endif
@@ -29,12 +30,12 @@ constexpr int kBlockN = MRA_BLOCK_N;  // keys per K/V tile
 #define MRA_ROW_BLOCKS 1
 #endif
 constexpr int kRowBlocks = MRA_ROW_BLOCKS;  // 32-row blocks per wave
-constexpr int kBlockM = kWaves * 32 * kRowBlocks;
 constexpr int kFp32BlockM = 64;
 constexpr size_t kWsAlign = 256;
-// Attention workgroups resident at once on an MI355X (256 CUs, two per CU).
+// Attention workgroups of w waves resident at once on an MI355X (256 CUs;
+// two per CU below 8 waves, one from 8).
 constexpr int kComputeUnits = 256;
-constexpr int kResidentSlots = kComputeUnits * (kWaves * kRowBlocks >= 8 ? 1 : 2);
+constexpr int resident_slots(int w) { return kComputeUnits * (w * kRowBlocks >= 8 ? 1 : 2); }
 // Workgroups the split tiles of the last wave are spread over: one per CU
 // (measured faster than filling both slots of every CU, which doubles the
 // partial results the merge pass reads).
@@ -92,7 +93,7 @@ int check_strides(const int64_t* st, int dtype) {
 // only) K' [B, H, S, D] bf16, then the fp32 split-tile records; every piece
 // starts 256-byte aligned.
 struct Plan {
-  int n;
+  int n, waves;
   int n_qt[MRA_MAX_GROUP];
   int tile_end[MRA_MAX_GROUP];
   int n_whole, n_split, nsplit;
@@ -117,12 +118,24 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.n = n;
+  // 8-wave workgroups (256 query rows, one per CU) when the problems hold at
+  // least 2.5 rounds of them, 4-wave ones (128 rows, two per CU) otherwise:
+  // 8 waves measured 1.4-4% faster on h36, ragged, long and 2048px, 0.7%
+  // slower at 1024px (2.25 rounds) and 27% slower at 512px (0.5 round)
+  int64_t tiles8 = 0;
+  for (int i = 0; i < n; ++i) {
+    const int qb = qbatch ? qbatch[i] : ds[i]->batch, ql = qlen ? qlen[i] : ds[i]->seq;
+    tiles8 += (int64_t)qb * ds[i]->heads * ((ql + 8 * 32 * kRowBlocks - 1) / (8 * 32 * kRowBlocks));
+  }
+  const int waves = MRA_WAVES ? MRA_WAVES : (2 * tiles8 >= 5 * (int64_t)resident_slots(8) ? 8 : 4);
+  const int bm = waves * 32 * kRowBlocks, slots = resident_slots(waves);
+  p.waves = waves;
   int tiles = 0, ktiles = 1 << 30;
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
     const mra_desc* d = ds[i];
     const int qb = qbatch ? qbatch[i] : d->batch, ql = qlen ? qlen[i] : d->seq;
-    p.n_qt[i] = (ql + kBlockM - 1) / kBlockM;
+    p.n_qt[i] = (ql + bm - 1) / bm;
     tiles += qb * d->heads * p.n_qt[i];
     p.tile_end[i] = tiles;
     ktiles = std::min(ktiles, (ql + kBlockN - 1) / kBlockN);
@@ -131,21 +144,21 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
     p.off_kp[i] = off;
     off += kprime_bytes(d);
   }
-  int r = tiles >= kResidentSlots ? tiles % kResidentSlots : tiles;
+  int r = tiles >= slots ? tiles % slots : tiles;
   int k = 1;
   // split when the last wave would leave at least half of the compute units
   // idle (a unit running one workgroup instead of two is not idle), or, after
   // whole waves, when it holds a few more tiles than there are units (a few
   // units would run two tiles while the rest run one: halves even them out;
   // measured on last waves of 192 to 416 tiles, it pays only in that band)
-  if (r > 0 && 4 * r <= kResidentSlots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
-  else if (tiles >= kResidentSlots && r > kComputeUnits && 4 * r <= 5 * kComputeUnits) k = std::min(2, ktiles);
+  if (r > 0 && 4 * r <= slots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
+  else if (tiles >= slots && r > kComputeUnits && 4 * r <= 5 * kComputeUnits) k = std::min(2, ktiles);
   if (k < 2) { r = 0; k = 1; }
   p.n_split = r;
   p.nsplit = k;
   p.n_whole = tiles - r;
   p.off_part = off;
-  const size_t rec_floats = (size_t)kRowBlocks * kWaves * 64 * (ds[0]->head_dim / 2 + 2);
+  const size_t rec_floats = (size_t)kRowBlocks * waves * 64 * (ds[0]->head_dim / 2 + 2);
   p.bytes = off + round_up((size_t)r * k * rec_floats * sizeof(float), kWsAlign);
   return p;
 }
@@ -200,20 +213,24 @@ hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int G>
-hipError_t launch_attend_group(const mra::Group<G>& g, int kpro, hipStream_t s) {
+template <int D, int W, int G>
+hipError_t launch_attend_waves(const mra::Group<G>& g, int kpro, hipStream_t s) {
   const unsigned grid = (unsigned)(g.n_whole + g.n_split * g.nsplit);
   if (kpro == MRA_KPRO_PREPASS)
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 0, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, W, kBlockN, kRowBlocks, 0, G>), dim3(grid), dim3(W * 64), 0, s, g);
   else if (kpro == MRA_KPRO_FUSED)
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 1, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, W, kBlockN, kRowBlocks, 1, G>), dim3(grid), dim3(W * 64), 0, s, g);
   else
-    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, kWaves, kBlockN, kRowBlocks, 2, G>), dim3(grid), dim3(kWaves * 64), 0, s, g);
+    hipLaunchKernelGGL((mra::attn_bf16_kernel<D, W, kBlockN, kRowBlocks, 2, G>), dim3(grid), dim3(W * 64), 0, s, g);
   if (g.n_split) {
-    const int64_t threads = (int64_t)g.n_split * kWaves * kRowBlocks * (D / 8) * 64;
-    hipLaunchKernelGGL((mra::split_merge_kernel<D, kWaves, kRowBlocks, G>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, g);
+    const int64_t threads = (int64_t)g.n_split * W * kRowBlocks * (D / 8) * 64;
+    hipLaunchKernelGGL((mra::split_merge_kernel<D, W, kRowBlocks, G>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, g);
   }
   return hipGetLastError();
+}
+template <int D, int G>
+hipError_t launch_attend_group(const mra::Group<G>& g, int kpro, int waves, hipStream_t s) {
+  return waves == 8 ? launch_attend_waves<D, 8>(g, kpro, s) : launch_attend_waves<D, 4>(g, kpro, s);
 }
 static_assert(sizeof(mra::Group<MRA_MAX_GROUP>) <= 4096, "kernel argument size");
 
@@ -237,11 +254,11 @@ hipError_t launch_attend(const Args* as, const Plan& p, void* workspace, int D, 
   if (p.n == 1) {
     mra::Group<1> g;
     make_group(g, as, p, workspace);
-    return D == 128 ? launch_attend_group<128>(g, kpro, s) : launch_attend_group<64>(g, kpro, s);
+    return D == 128 ? launch_attend_group<128>(g, kpro, p.waves, s) : launch_attend_group<64>(g, kpro, p.waves, s);
   }
   mra::Group<MRA_MAX_GROUP> g;
   make_group(g, as, p, workspace);
-  return D == 128 ? launch_attend_group<128>(g, kpro, s) : launch_attend_group<64>(g, kpro, s);
+  return D == 128 ? launch_attend_group<128>(g, kpro, p.waves, s) : launch_attend_group<64>(g, kpro, p.waves, s);
 }
 
 // qlen: rows per item (a.S for the padded layout, the longest item for a

@@ -173,11 +173,20 @@ def test_workspace_sizes(lib):
                                  kprologue="fused")) == 4096 * 64 * 8
     assert B.workspace_size(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12))) == 0
     assert B.workspace_size(desc(section=(1, 2, 3))) == 0          # invalid -> 0
-    rec = 256 * (128 // 2 + 2) * 4                                 # one part's records
-    # 36 heads: 1296 tiles leave 272 after two waves, a few more than the 256
-    # compute units: cut into 2 key ranges
+    rec4 = 4 * 64 * (128 // 2 + 2) * 4                             # one part's records, 4 waves
+    rec8 = 8 * 64 * (128 // 2 + 2) * 4                             # 8 waves
+    # 8-wave workgroups (256 rows, one per CU) from 2.5 rounds of them: 36
+    # heads at 4608 tokens make 648, whose 136-tile last wave is not cut
     h36 = desc(batch=1, seq=4608, heads=36, text_pad=512)
-    assert B.workspace_size(h36) == table + 4608 * 36 * 128 * 2 + 272 * 2 * rec
+    assert B.workspace_size(h36) == table + 4608 * 36 * 128 * 2
+    # 12800 tokens: 1600 tiles of 256 rows leave 64, cut into 4 key ranges
+    lng = desc(batch=1, seq=12800, heads=32, text_pad=512)
+    assert B.workspace_size(lng) == 12800 * 64 * 8 + 12800 * 32 * 128 * 2 + 64 * 4 * rec8
+    # 4-wave problems (under 2.5 rounds of 256-row tiles): 2 x 196 heads x
+    # 200 tokens make 784 tiles of 128 rows, a 272-tile last wave, a few more
+    # than the 256 compute units: cut into 2 key ranges
+    d3 = desc(batch=2, seq=200, heads=196, text_pad=32)
+    assert B.workspace_size(d3) == 2 * 200 * 64 * 8 + 2 * 200 * 196 * 128 * 2 + 272 * 2 * rec4
     # 928 tiles leave 416: not cut; 704 tiles leave 192: not cut
     for seq, heads in ((3712, 32), (2816, 32)):
         d2 = desc(batch=1, seq=seq, heads=heads, text_pad=512)
@@ -242,9 +251,10 @@ def test_group_workspace_is_the_sum_of_its_parts(lib):
     cond = desc(batch=1, seq=4608, heads=32, text_pad=512)
     uncond = desc(batch=1, seq=4096, heads=32, text_pad=0)
     # per problem: rotary table + K'; then the split records of the combined
-    # grid: 1152 + 1024 = 2176 tiles leave 128 for the last wave -> 2 parts
+    # grid: 576 + 512 = 1088 tiles of 256 rows (8-wave workgroups, over 2.5
+    # rounds) leave 64 for the last wave -> 4 parts
     per = [s * 64 * 8 + s * 32 * 128 * 2 for s in (4608, 4096)]
-    split = 128 * 2 * 256 * (128 // 2 + 2) * 4
+    split = 64 * 4 * 512 * (128 // 2 + 2) * 4
     assert B.group_workspace_size([cond, uncond]) == sum(per) + split
     # a group of one is the plain call
     assert B.group_workspace_size([cond]) == B.workspace_size(cond)

@@ -235,15 +235,20 @@ def test_config_512px_full():
 
 
 @pytest.mark.parametrize("shape", [
-    # 2 x 96 heads x 3 tiles = 576 tiles: a 64-tile last wave cut into 4 key ranges
+    # 4-wave workgroups: 2 x 96 heads x 3 tiles of 128 rows = 576 tiles, a
+    # 64-tile last wave cut into 4 key ranges
     dict(batch=2, heads=96, text_pad=48, grid_h=12, grid_w=21, text_lens=(20, 48)),
-    # 2 x 392 heads x 1 tile = 784 tiles: a 272-tile last wave (more tiles
-    # than compute units) cut into 2 key ranges
+    # 4-wave workgroups: 2 x 196 heads x 2 tiles = 784 tiles, a 272-tile last
+    # wave (more tiles than compute units) cut into 2 key ranges
+    dict(batch=2, heads=196, text_pad=32, grid_h=12, grid_w=14, text_lens=(32, 9)),
+    # 8-wave workgroups (784 tiles of 256 rows): a 16-tile last wave cut into
+    # 2 key ranges (two key tiles per row)
     dict(batch=2, heads=392, text_pad=28, grid_h=8, grid_w=9, text_lens=(28, 5)),
 ])
 def test_tail_split_full(shape):
     """Every output of a problem whose last wave of query tiles is cut into key
-    ranges (and merged by the log-sum-exp rule), under each split rule."""
+    ranges (and merged by the log-sum-exp rule), under each split rule and
+    both workgroup sizes."""
     w = make_workload(shape["batch"], shape["heads"], 128, (16, 24, 24), shape["text_pad"], shape["grid_h"],
                       shape["grid_w"], text_lens=shape["text_lens"], dtype="bf16", seed=390 + shape["heads"])
     say(f"case: tail split {w.shape}")
