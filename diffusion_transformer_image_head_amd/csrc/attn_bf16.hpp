@@ -28,9 +28,9 @@
 // the order that makes each lane's 16 S^T values 16 consecutive keys, so the P
 // fragment feeds P.V directly. K' and V are double-buffered: after each
 // tile's barrier the loads of tile t+1 are issued, then Q.K'(t), the softmax
-// and P.V(t) run; the two waves sharing a SIMD (two workgroups per CU) overlap
-// one's matrix work with the other's exponentials, and a wave raises its issue
-// priority for its P.V run.
+// and P.V(t) run; the two waves sharing a SIMD (two 4-wave workgroups per
+// CU, or one 8-wave workgroup) overlap one's matrix work with the other's
+// exponentials, and a wave raises its issue priority for its P.V run.
 //
 // Numerics: Q' is rounded to bf16 already multiplied by softmax_scale*log2(e),
 // so S^T is in log2 units; the S^T accumulators start at -m (the running row
