@@ -111,6 +111,36 @@ def test_bf16_peaked():
     assert ma <= PEAKED_BARS[0] and rr <= PEAKED_BARS[1]
 
 
+def test_bf16_peaked_8wave_sampled():
+    """The online max and lazy rescale in 8-wave workgroups: 40 heads x 4096
+    tokens is 640 tiles of 256 rows (the plan's 8-wave size), with gammas x3
+    so the logit bound is too loose for the fixed max. Sampled rows of every
+    head against the oracle, with the peaked bars, which are checked here to
+    sit above the bf16 rounding floor of Q' and K' on the same rows."""
+    import oracle.reference as R
+    from diffusion_transformer_image_head_amd.workloads import round_to_bf16
+    from tests.gpu_util import errors
+    from tests.test_tolerance import PEAKED_BARS
+    w = make_workload(1, 40, 128, (16, 24, 24), 256, 60, 64, dtype="bf16", seed=330)
+    w.gamma_q = w.gamma_q * 3
+    w.gamma_k = w.gamma_k * 3
+    say("case: bf16 peaked, 8-wave workgroups, sampled rows")
+    out, _ = run_gpu(w)
+    rows = sample_rows(w, n=48)
+    ref_o, _ = run_oracle(w, rows=rows)
+    qr = R.mrope(R.rms_norm(w.q, w.gamma_q, w.eps), w.pos, w.section, w.theta)
+    kr = R.mrope(R.rms_norm(w.k, w.gamma_k, w.eps), w.pos, w.section, w.theta)
+    rb = lambda x: round_to_bf16(x.astype(np.float32)).astype(np.float64)  # noqa: E731
+    valid = R.valid_tokens(1, w.q.shape[1], w.text_pad, w.seq_lens)
+    floor_o, _ = R.attention(rb(qr), rb(kr), w.v, valid, 1.0 / np.sqrt(128.0), rows=rows)
+    fa, fr = errors(floor_o, ref_o)
+    assert fa * 1.2 < PEAKED_BARS[0] and fr * 1.2 < PEAKED_BARS[1], (fa, fr)
+    ma, rr = errors(out[:, rows], ref_o)
+    say(f"  parity: max_abs={ma:.3e} rel_rms={rr:.3e} (floor {fa:.3e} / {fr:.3e}, bars {PEAKED_BARS})")
+    assert np.isfinite(out).all()
+    assert ma <= PEAKED_BARS[0] and rr <= PEAKED_BARS[1]
+
+
 # ------------------------------------------------------------------ conventions
 # a gamma per head ([H, D]) and interleaved rotary pairs (2j, 2j + 1), alone
 # and together, on multi-tile ragged shapes, D = 64, and the fp32 path
