@@ -206,7 +206,9 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
  * only. desc->seq is the total token count, desc->text_pad must be 0
  * (MRA_ERR_SHAPE), the batch strides are not used, pos_thw is [seq, 3] and
  * lse [H, seq]. cu_seqlens is a device [batch + 1] int32 array, read on the
- * device and clamped into [0, seq]; max_seqlen (0..seq, else MRA_ERR_SHAPE)
+ * device and clamped into [0, seq]; it must be non-decreasing (an entry below
+ * its predecessor makes that sequence empty, and sequences that overlap
+ * write the same rows in an unspecified order); max_seqlen (0..seq, else MRA_ERR_SHAPE)
  * must be at least every sequence's length: rows past max_seqlen of a longer
  * sequence are not computed. Tokens outside every sequence are not written. */
 size_t mrope_attn_varlen_workspace_size(const mra_desc* desc, int32_t max_seqlen);
