@@ -363,7 +363,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="1024px",
-                    choices=["512px", "1024px", "ragged", "long", "h36", "2048px", "cfg1024"],
+                    choices=["512px", "1024px", "ragged", "long", "h36", "2048px", "cfg1024", "h4"],
                     help="cfg1024: one guided step, the 1024px conditional pass and its "
                          "image-only unconditional pass in one grouped call")
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])

@@ -153,6 +153,12 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
   // measured on last waves of 192 to 416 tiles, it pays only in that band)
   if (r > 0 && 4 * r <= slots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
   else if (tiles >= slots && r > kComputeUnits && 4 * r <= 5 * kComputeUnits) k = std::min(2, ktiles);
+  // a single wave too full for the first rule but at most 3/5 of the slots
+  // (say one GPU's 4 or 8 heads of a head-sharded layer): every tile in 3 key
+  // ranges, when each range keeps at least 24 key tiles (measured at 4608
+  // tokens: 144 tiles 90.6 -> 66.3 us, 288 tiles 129.6 -> 119.0 us; 2 or 4
+  // ranges less; 512px, 20 key tiles, loses with any cut)
+  else if (tiles < slots && 5 * r <= 3 * slots && ktiles >= 3 * 24) k = std::min(3, mra::kMaxSplit);
   if (k < 2) { r = 0; k = 1; }
   p.n_split = r;
   p.nsplit = k;

@@ -51,6 +51,10 @@ CONFIGS = {
     "conv": dict(batch=2, heads=32, head_dim=128, section=(16, 24, 24), text_pad=512,
                  text_lens=(77, 512), grid_h=64, grid_w=64, sigma=1.0, dtype="bf16", seed=7,
                  gamma_per_head=True, rope_pairs="interleaved"),
+    # one GPU's share of the 1024px layer when its 32 heads are split over 8
+    # GPUs (heads need no exchange): 4 heads x 4608 tokens
+    "h4": dict(batch=1, heads=4, head_dim=128, section=(16, 24, 24), text_pad=512,
+               text_lens=None, grid_h=64, grid_w=64, sigma=1.0, dtype="bf16", seed=8),
 }
 
 

@@ -264,6 +264,14 @@ def test_config_512px_full():
     _full_check(config_workload("512px"))
 
 
+def test_config_h4_full():
+    """One GPU's share of a head-sharded 1024px layer (4 heads x 4608
+    tokens): a single wave of 144 tiles, every tile cut into 3 key ranges.
+    Every output against the oracle."""
+    say("case: h4 config (4 heads x 4608 tokens), all outputs")
+    _full_check(config_workload("h4"))
+
+
 @pytest.mark.parametrize("shape", [
     # 4-wave workgroups: 2 x 96 heads x 3 tiles of 128 rows = 576 tiles, a
     # 64-tile last wave cut into 4 key ranges
