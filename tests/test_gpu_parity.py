@@ -201,6 +201,27 @@ def test_uniform_v_exact():
     assert np.all(out[~valid] == 0)
 
 
+def test_scale_invariance():
+    """The QK-RMSNorm makes the output independent of the scale of q and k.
+    With eps = 0 and power-of-two scales (exact in bf16) the normalisation
+    only shifts exponents (the rsqrt of 4x is half that of x, exactly), so
+    q x 2 and k x 1/4 give the unscaled call's output bit for bit, and both
+    match the oracle."""
+    say("case: scale invariance")
+    w = make_workload(2, 3, 128, (16, 24, 24), 48, 11, 13, text_lens=(5, 48), dtype="bf16", seed=345)
+    w.eps = 0.0
+    a, _ = run_gpu(w)
+    ref, _ = run_oracle(w)
+    check_parity(a, ref, "bf16", "unscaled")
+    w.q = w.q * 2.0
+    w.k = w.k * 0.25
+    b, _ = run_gpu(w)
+    d = float(np.max(np.abs(a - b)))
+    say(f"  max |out(2q, k/4) - out(q, k)| = {d:.3e}")
+    assert d == 0.0
+    check_parity(b, ref, "bf16", "scaled")
+
+
 def test_single_valid_token():
     say("case: single valid token")
     w = make_workload(1, 2, 128, (16, 24, 24), 3, 0, 0, text_lens=(1,), dtype="bf16", seed=341)
