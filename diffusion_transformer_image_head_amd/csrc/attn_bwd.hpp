@@ -212,54 +212,40 @@ __device__ __forceinline__ void dgamma_partial(float (&dg)[D / 32][16], float* r
   }
 }
 
-// dK and dV: one workgroup per (batch, head, 128 keys), 32 keys per wave;
+// LDS of a dK/dV workgroup: stage p holds Q'' (q[p]), dO (o[p]) and the
+// (l2, D) pairs (l[p]) of one query tile, each its own object so that a
+// stage's reads never wait on another stage's loads; vk holds the V rows of
+// the workgroup's 128 keys (row = key, chunk c at c ^ (row & 15)), read back
+// as B operands each tile instead of held in registers; red is the gamma
+// reduction's buffer.
+struct DkdvLds {
+  char* q[4];
+  char* o[4];
+  float* l[4];
+  char* vk;
+  float* red;
+};
+
+// dK and dV of workgroup `tile`: (batch, head, 128 keys), 32 keys per wave;
 // query tiles of 32 stream through LDS. INTER: interleaved rotary pairs
-// (2j, 2j + 1) in the epilogue's inverse rotation. MODE 0 computes both (one
-// wave per SIMD: dK, dV and K' take most of the registers; four stages);
-// MODE 1 only dV (S, P, dV) and MODE 2 only dK (S, P, dP, dS, dK): each of
-// those recomputes S but fits two waves per SIMD (two stages).
+// (2j, 2j + 1) in the epilogue's inverse rotation. MODE 0: both, 1: dV only,
+// 2: dK only.
 template <int D, bool INTER, int MODE>
-__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs g) {
+__device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, const DkdvLds& sm) {
   constexpr int KC = D / 16, DB = D / 32, BQ = 32, TILEB = BQ * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
   constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
   constexpr int NST = MODE == 0 ? 4 : 2;  // pipeline stages: NST - 1 query tiles in flight
   constexpr int LOADS = 2 * RUNS + 1;  // direct loads per wave per tile
   static_assert(D == 128, "the backward kernels are written for head_dim 128");
-  // Stage p holds Q'' (Qp), dO (Op) and the (l2, D) pairs (Lp) of one query
-  // tile; separate objects so a stage's reads never wait on another's loads.
-  __shared__ __attribute__((aligned(1024))) char Q0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char Q1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char Q2[TILEB];
-  __shared__ __attribute__((aligned(1024))) char Q3[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O2[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O3[TILEB];
-  __shared__ __attribute__((aligned(256))) float L0[2 * BQ];
-  __shared__ __attribute__((aligned(256))) float L1[2 * BQ];
-  __shared__ __attribute__((aligned(256))) float L2[2 * BQ];
-  __shared__ __attribute__((aligned(256))) float L3[2 * BQ];
-  // V rows of the workgroup's 128 keys (row = key, chunk c at c ^ (row & 15)):
-  // read back as B operands each tile instead of held in registers
-  __shared__ __attribute__((aligned(1024))) char Vk[DO_DK ? 128 * D * 2 : 16];
-  __shared__ float red[4 * D];
-  auto qb = [&](auto par) -> char* {
-    constexpr int p = decltype(par)::value;
-    if constexpr (p == 0) return Q0; else if constexpr (p == 1) return Q1; else if constexpr (p == 2) return Q2; else return Q3;
-  };
-  auto ob = [&](auto par) -> char* {
-    constexpr int p = decltype(par)::value;
-    if constexpr (p == 0) return O0; else if constexpr (p == 1) return O1; else if constexpr (p == 2) return O2; else return O3;
-  };
-  auto lb = [&](auto par) -> float* {
-    constexpr int p = decltype(par)::value;
-    if constexpr (p == 0) return L0; else if constexpr (p == 1) return L1; else if constexpr (p == 2) return L2; else return L3;
-  };
+  char* const Vk = sm.vk;
+  float* const red = sm.red;
+  auto qb = [&](auto par) -> char* { return sm.q[decltype(par)::value]; };
+  auto ob = [&](auto par) -> char* { return sm.o[decltype(par)::value]; };
+  auto lb = [&](auto par) -> float* { return sm.l[decltype(par)::value]; };
 
   const Args& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 31, hf = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int kt = tile % g.n_t, bh = tile / g.n_t;
   const int head = bh % a.H, b = bh / a.H;
   // item b: S tokens from token tok0 of slice bl (packed sequences: one
@@ -486,22 +472,54 @@ __global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArg
   dgamma_partial<D>(dg, red, g.dgk_part + (int64_t)tile * D, wave, lane);
 }
 
-// dQ: one workgroup per (batch, head, 128 queries), 32 per wave; key tiles of
-// 32 (K' and V) stream through double-buffered LDS. INTER as for dK/dV.
+// MODE 0 computes dK and dV (one wave per SIMD: dK, dV and K' take most of
+// the registers; four stages); MODE 1 only dV (S, P, dV) and MODE 2 only dK
+// (S, P, dP, dS, dK): each of those recomputes S but fits two waves per SIMD
+// (two stages).
+template <int D, bool INTER, int MODE>
+__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs g) {
+  constexpr int TILEB = 32 * D * 2, NST = MODE == 0 ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) char Q0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Q1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char Q2[NST == 4 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char Q3[NST == 4 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char O0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char O1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char O2[NST == 4 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char O3[NST == 4 ? TILEB : 16];
+  __shared__ __attribute__((aligned(256))) float L0[64];
+  __shared__ __attribute__((aligned(256))) float L1[64];
+  __shared__ __attribute__((aligned(256))) float L2[64];
+  __shared__ __attribute__((aligned(256))) float L3[64];
+  __shared__ __attribute__((aligned(1024))) char Vk[MODE != 1 ? 128 * D * 2 : 16];
+  __shared__ float red[4 * D];
+  const DkdvLds sm{{Q0, Q1, Q2, Q3}, {O0, O1, O2, O3}, {L0, L1, L2, L3}, Vk, red};
+  bwd_dkdv_body<D, INTER, MODE>(g, xcd_remap(blockIdx.x, gridDim.x), sm);
+}
+
+// LDS of a dQ workgroup: K' (k[p]) and V (v[p]) of key tile stage p, the
+// gamma reduction's buffer.
+struct DqLds {
+  char* k[2];
+  char* v[2];
+  float* red;
+};
+
+// dQ of workgroup `tile`: (batch, head, 128 queries), 32 per wave; key tiles
+// of 32 (K' and V) stream through double-buffered LDS. INTER as for dK/dV.
 template <int D, bool INTER>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
+__device__ __forceinline__ void bwd_dq_body(const BwdArgs& g, const int tile, const DqLds& sm) {
   constexpr int KC = D / 16, DB = D / 32, BK = 32, TILEB = BK * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
   static_assert(D == 128, "the backward kernels are written for head_dim 128");
-  __shared__ __attribute__((aligned(1024))) char K0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char K1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char V0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char V1[TILEB];
-  __shared__ float red[4 * D];
+  char* const K0 = sm.k[0];
+  char* const K1 = sm.k[1];
+  char* const V0 = sm.v[0];
+  char* const V1 = sm.v[1];
+  float* const red = sm.red;
 
   const Args& a = g.a;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 31, hf = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int qtile = tile % g.n_t, bh = tile / g.n_t;
   const int head = bh % a.H, b = bh / a.H;
   // item b: S tokens from token tok0 of slice bl, as in the dK/dV kernel
@@ -645,6 +663,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
                            hf, dg);
   }
   dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)tile * D, wave, lane);
+}
+
+template <int D, bool INTER>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
+  constexpr int TILEB = 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char K0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char K1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char V0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char V1[TILEB];
+  __shared__ float red[4 * D];
+  const DqLds sm{{K0, K1}, {V0, V1}, red};
+  bwd_dq_body<D, INTER>(g, xcd_remap(blockIdx.x, gridDim.x), sm);
+}
+
+// dK, dQ and dV in one launch: the three are independent, and one grid of
+// 3 x n_wg workgroups leaves one partial round of workgroups at its end where
+// three launches of n_wg leave one each. Workgroup i runs on XCD i % 8 (the
+// dispatcher's round robin); XCD x takes, in order, its contiguous share of
+// the dK tiles, then of the dQ tiles, then of the dV tiles (the lightest role
+// last), each share ceil(n_wg / 8) tiles (the grid is 24 x that; workgroups
+// past the last tile exit). The roles share one set of LDS objects, so the
+// kernel needs the largest role's LDS, not their sum.
+template <int D, bool INTER>
+__global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs g) {
+  constexpr int TILEB = 32 * D * 2;
+  __shared__ __attribute__((aligned(1024))) char B0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char B1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char B2[TILEB];
+  __shared__ __attribute__((aligned(1024))) char B3[TILEB];
+  __shared__ __attribute__((aligned(256))) float L0[64];
+  __shared__ __attribute__((aligned(256))) float L1[64];
+  __shared__ __attribute__((aligned(1024))) char Vk[128 * D * 2];
+  __shared__ float red[4 * D];
+  const int n_wg = g.a.B * g.a.H * g.n_t;
+  const int per = (n_wg + 7) / 8;
+  const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int role = j / per, tile = x * per + j % per;
+  if (tile >= n_wg) return;
+  if (role == 1) {
+    const DqLds sm{{B0, B1}, {B2, B3}, red};
+    bwd_dq_body<D, INTER>(g, tile, sm);
+  } else {
+    const DkdvLds sm{{B0, B1, nullptr, nullptr}, {B2, B3, nullptr, nullptr}, {L0, L1, nullptr, nullptr}, Vk, red};
+    if (role == 0) bwd_dkdv_body<D, INTER, 2>(g, tile, sm);
+    else bwd_dkdv_body<D, INTER, 1>(g, tile, sm);
+  }
 }
 
 // gamma gradient = sum of the workgroup partials in a fixed order. The

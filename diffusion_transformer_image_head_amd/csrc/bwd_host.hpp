@@ -88,26 +88,36 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
   // the matrix-core kernels work per item
   g.a.B = nseq;
   g.a.cu_seqlens = cu_seqlens;
-  // dK and dV: one fused kernel, or (MRA_BWD_SPLIT) two that each recompute S
+  // dK, dQ and dV: one launch of the three roles (MRA_BWD_FUSED), or three
+  // launches; with three, dK and dV come from one kernel that computes both
+  // (MRA_BWD_SPLIT 0) or two that each recompute S
+#ifndef MRA_BWD_FUSED
+#define MRA_BWD_FUSED 1
+#endif
 #ifndef MRA_BWD_SPLIT
 #define MRA_BWD_SPLIT 1
 #endif
-  if (g.a.inter) {
+  const unsigned nwg = (unsigned)p.n_wg;
+  if (MRA_BWD_FUSED) {
+    const unsigned grid = 24u * ((nwg + 7u) / 8u);
+    if (g.a.inter) hipLaunchKernelGGL((mra::bwd_fused_kernel<128, true>), dim3(grid), dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((mra::bwd_fused_kernel<128, false>), dim3(grid), dim3(256), 0, s, g);
+  } else if (g.a.inter) {
     if (MRA_BWD_SPLIT) {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 1>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 2>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 1>), dim3(nwg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 2>), dim3(nwg), dim3(256), 0, s, g);
     } else {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 0>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 0>), dim3(nwg), dim3(256), 0, s, g);
     }
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3(nwg), dim3(256), 0, s, g);
   } else {
     if (MRA_BWD_SPLIT) {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 1>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 2>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 1>), dim3(nwg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 2>), dim3(nwg), dim3(256), 0, s, g);
     } else {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 0>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 0>), dim3(nwg), dim3(256), 0, s, g);
     }
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3((unsigned)p.n_wg), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3(nwg), dim3(256), 0, s, g);
   }
   if (dgamma_q || dgamma_k) {
     // per-tile partials are laid out [nseq, H, n_t, D]: a shared gamma sums

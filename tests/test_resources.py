@@ -21,7 +21,8 @@ from diffusion_transformer_image_head_amd import build as B
 # registers outside its loop; the split dK and dV kernels must not spill.
 SPILL_CEILING = {"bwd_dkdv_kernel": 12}
 # two attention workgroups per CU need each wave within 256 registers
-VGPR_CEILING = {"attn_bf16_kernel": 256, "bwd_dq_kernel": 256, "qkv_proj_kernel": 256}
+VGPR_CEILING = {"attn_bf16_kernel": 256, "bwd_dq_kernel": 256, "bwd_fused_kernel": 256,
+                "qkv_proj_kernel": 256}
 
 
 @pytest.fixture(scope="module")
@@ -53,7 +54,7 @@ def test_every_kernel_is_reported(kernels):
     kinds = {_kind(k) for k in kernels}
     for k in ("attn_bf16_kernel", "split_merge_kernel", "k_prologue_kernel", "rope_table_kernel",
               "attn_fp32_kernel", "bwd_delta_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel",
-              "bwd_dgamma_kernel", "qkv_proj_kernel"):
+              "bwd_dgamma_kernel", "bwd_fused_kernel", "qkv_proj_kernel"):
         assert k in kinds, k
 
 
