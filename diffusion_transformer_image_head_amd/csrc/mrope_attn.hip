@@ -119,15 +119,22 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
   std::memset(&p, 0, sizeof(p));
   p.n = n;
   // 8-wave workgroups (256 query rows, one per CU) when the problems hold at
-  // least 2.5 rounds of them, 4-wave ones (128 rows, two per CU) otherwise:
-  // 8 waves measured 1.4-4% faster on h36, ragged, long and 2048px, 0.7%
-  // slower at 1024px (2.25 rounds) and 27% slower at 512px (0.5 round)
+  // least 2.5 rounds of them, or one partial round that the third split rule
+  // below cuts into 3 key ranges; 4-wave ones (128 rows, two per CU)
+  // otherwise. 8 waves measured 1.4-4% faster on h36, ragged, long and
+  // 2048px, 6% on 4 heads and 1.5% on 8 heads at 4608 tokens (a cut single
+  // round either way), 0.7% slower at 1024px (2.25 rounds) and 27% slower at
+  // 512px (0.5 round, too few key tiles to cut)
   int64_t tiles8 = 0;
+  int kt_min = 1 << 30;
   for (int i = 0; i < n; ++i) {
     const int qb = qbatch ? qbatch[i] : ds[i]->batch, ql = qlen ? qlen[i] : ds[i]->seq;
     tiles8 += (int64_t)qb * ds[i]->heads * ((ql + 8 * 32 * kRowBlocks - 1) / (8 * 32 * kRowBlocks));
+    kt_min = std::min(kt_min, (ql + kBlockN - 1) / kBlockN);
   }
-  const int waves = MRA_WAVES ? MRA_WAVES : (2 * tiles8 >= 5 * (int64_t)resident_slots(8) ? 8 : 4);
+  const int64_t s8 = resident_slots(8);
+  const bool cut_round8 = 4 * tiles8 > s8 && 5 * tiles8 <= 3 * s8 && kt_min >= 3 * 24;
+  const int waves = MRA_WAVES ? MRA_WAVES : ((2 * tiles8 >= 5 * s8 || cut_round8) ? 8 : 4);
   const int bm = waves * 32 * kRowBlocks, slots = resident_slots(waves);
   p.waves = waves;
   int tiles = 0, ktiles = 1 << 30;

@@ -187,10 +187,12 @@ def test_workspace_sizes(lib):
     # than the 256 compute units: cut into 2 key ranges
     d3 = desc(batch=2, seq=200, heads=196, text_pad=32)
     assert B.workspace_size(d3) == 2 * 200 * 64 * 8 + 2 * 200 * 196 * 128 * 2 + 272 * 2 * rec4
-    # one wave of 4 x 36 = 144 tiles (4 heads at 4608 tokens, 72 key tiles
-    # each): every tile in 3 key ranges; 512px (240 tiles of 20 key tiles): none
+    # one partial round of 4 x 18 = 72 tiles of 256 rows (4 heads at 4608
+    # tokens, 72 key tiles each): 8 waves, every tile in 3 key ranges (the
+    # same bytes as 144 tiles of 128 rows); 512px (240 tiles of 128 rows, 20
+    # key tiles): 4 waves, no cut
     h4 = desc(batch=1, seq=4608, heads=4, text_pad=512)
-    assert B.workspace_size(h4) == table + 4608 * 4 * 128 * 2 + 144 * 3 * rec4
+    assert B.workspace_size(h4) == table + 4608 * 4 * 128 * 2 + 72 * 3 * rec8
     p512 = desc(batch=1, seq=1280, heads=24, text_pad=256)
     assert B.workspace_size(p512) == 1280 * 64 * 8 + 1280 * 24 * 128 * 2
     # 928 tiles leave 416: not cut; 704 tiles leave 192: not cut
