@@ -13,11 +13,13 @@
 // then the transpose rotation and the RMSNorm backward turn dQ', dK' into dq,
 // dk and the gamma gradients.
 //
-// Kernels: bwd_delta_kernel (D and l2 per row), bwd_dkdv_kernel (one
-// workgroup per 128 keys, 32 per wave, streaming 32-query tiles of Q'' and
-// dO through LDS), bwd_dq_kernel (one workgroup per 128 queries, streaming
-// 32-key tiles of K' and V), bwd_dgamma_kernel (fixed-order sum of the
-// per-workgroup gamma partials). The dk/dv and dq kernels work per item
+// Kernels: bwd_delta_kernel (D and l2 per row); bwd_fused_kernel, one launch
+// of three independent roles: dK and dV (bwd_dkdv_body: one workgroup per 128
+// keys, 32 per wave, streaming 32-query tiles of Q'' and dO through LDS) and
+// dQ (bwd_dq_body: one workgroup per 128 queries, streaming 32-key tiles of
+// K' and V), also launchable apart as bwd_dkdv_kernel and bwd_dq_kernel;
+// bwd_dgamma_kernel (fixed-order sum of the per-workgroup gamma partials).
+// The dk/dv and dq roles work per item
 // (seq_view): a padded batch item, or one sequence of a packed layout whose
 // streams start at the sequence's first token and end with its last, so a
 // sequence only sees its own tokens. All matrix products use
@@ -713,23 +715,27 @@ __global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs g) {
 
 // gamma gradient = sum of the workgroup partials in a fixed order. The
 // partials of tile (b, h, t) sit at row (b * H + h) * n_t + t. Workgroup
-// (which, h) -- which 0: gamma_q, 1: gamma_k -- sums the n partials of its
-// gradient row h: partial i < n is row (i / run) * stride + h * run + i % run
-// (a shared [D] gamma: one row, run = n = every tile, stride 0; an [H, D]
-// gamma: row h, run = n_t, stride = H * n_t, n = B * n_t). Thread (grp, d)
-// of 8 x D sums partials grp, grp + 8, ... with four interleaved
-// accumulators, then the 8 x 4 sums are added in a fixed order.
+// (which, h, chunk) -- which 0: gamma_q, 1: gamma_k -- sums dims
+// [chunk * DC, chunk * DC + DC) of the n partials of its gradient row h:
+// partial i < n is row (i / run) * stride + h * run + i % run (a shared [D]
+// gamma: one row, run = n = every tile, stride 0; an [H, D] gamma: row h,
+// run = n_t, stride = H * n_t, n = B * n_t). Thread (grp, d) of G x DC sums
+// partials grp, grp + G, ... with four interleaved accumulators, then the
+// G x 4 sums are added in a fixed order.
 template <int D>
-__global__ __launch_bounds__(8 * D) void bwd_dgamma_kernel(const float* part_q, const float* part_k, int n,
+__global__ __launch_bounds__(1024) void bwd_dgamma_kernel(const float* part_q, const float* part_k, int n,
                                                           int run, int64_t stride, float* out_q,
                                                           float* out_k) {
-  __shared__ float red[8][D];
-  const int which = blockIdx.x & 1, h = blockIdx.x >> 1;
+  constexpr int DC = 32, G = 1024 / DC, NC = D / DC;
+  static_assert(D % DC == 0, "head_dim is a multiple of the dim chunk");
+  __shared__ float red[G][DC];
+  const int chunk = blockIdx.x % NC, rest = blockIdx.x / NC;
+  const int which = rest & 1, h = rest >> 1;
   const float* part = (which ? part_k : part_q) + (int64_t)h * run * D;
   float* out = which ? out_k : out_q;
   if (!out) return;
   out += (int64_t)h * D;
-  const int d = threadIdx.x % D, grp = threadIdx.x / D;
+  const int d = chunk * DC + threadIdx.x % DC, grp = threadIdx.x / DC;
   // a shared gamma sums every partial in order (run == n: no division)
   auto at = [&](int i) {
     const int64_t r = run == n ? i : (int64_t)(i / run) * stride + i % run;
@@ -737,17 +743,17 @@ __global__ __launch_bounds__(8 * D) void bwd_dgamma_kernel(const float* part_q, 
   };
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int i = grp;
-  for (; i + 24 < n; i += 32) {
+  for (; i + 3 * G < n; i += 4 * G) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += at(i + 8 * u);
+    for (int u = 0; u < 4; ++u) acc[u] += at(i + G * u);
   }
-  for (int u = 0; i < n; i += 8, ++u) acc[u & 3] += at(i);
-  red[grp][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  for (int u = 0; i < n; i += G, ++u) acc[u & 3] += at(i);
+  red[grp][threadIdx.x % DC] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   __syncthreads();
   if (grp == 0) {
     float t = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) t += red[g][d];
+#pragma unroll 8
+    for (int g = 0; g < G; ++g) t += red[g][threadIdx.x];
     out[d] = t;
   }
 }

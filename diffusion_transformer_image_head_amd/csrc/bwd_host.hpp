@@ -126,7 +126,7 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
     const int n = ph ? nseq * p.n_t : p.n_wg;
     const int run = ph ? p.n_t : p.n_wg;
     const int64_t stride = ph ? (int64_t)d->heads * p.n_t : 0;
-    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2u * (ph ? d->heads : 1)), dim3(8 * 128), 0, s,
+    hipLaunchKernelGGL(mra::bwd_dgamma_kernel<128>, dim3(2u * (ph ? d->heads : 1) * (128 / 32)), dim3(1024), 0, s,
                        (const float*)g.dgq_part, (const float*)g.dgk_part, n, run, stride, dgamma_q,
                        dgamma_k);
   }
