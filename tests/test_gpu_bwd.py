@@ -138,6 +138,21 @@ def test_bwd_1024px_two_heads():
     check_bwd(got, ref, "1024px heads 0,17")
 
 
+def test_bwd_1024px_all_heads():
+    """The benchmark's backward as it is timed: the 1024px shape with all 32
+    heads, 1152 workgroups per gradient role in one launch (every XCD's share
+    of every role) and the shared gammas' 1152 partials; every output
+    compared (the oracle loops over the heads, about half a minute)."""
+    say("case: bwd 1024px all 32 heads")
+    w = config_workload("1024px")
+    do = dout_for(w)
+    got = run_bwd(w, do)
+    say("  gpu done; oracle running")
+    ref = oracle_bwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens, do,
+                     text_pad=w.text_pad, section=w.section)
+    check_bwd(got, ref, "1024px all heads")
+
+
 def test_bwd_ragged_items():
     """Ragged true text lengths at a mid-size shape, every output compared."""
     say("case: bwd ragged mid-size")
