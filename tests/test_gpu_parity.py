@@ -285,10 +285,18 @@ def test_config_512px_full():
     _full_check(config_workload("512px"))
 
 
+def test_config_1024px_full():
+    """The benchmark's forward as it is timed: the 1024px shape with all 32
+    heads (1152 query tiles of 128 rows, a 128-tile last wave cut into 2 key
+    ranges). Every output against the oracle (a few seconds of it)."""
+    say("case: 1024px config, all outputs")
+    _full_check(config_workload("1024px"))
+
+
 def test_config_h4_full():
     """One GPU's share of a head-sharded 1024px layer (4 heads x 4608
-    tokens): a single wave of 144 tiles, every tile cut into 3 key ranges.
-    Every output against the oracle."""
+    tokens): a single partial round of 72 tiles of 256 rows, every tile cut
+    into 3 key ranges. Every output against the oracle."""
     say("case: h4 config (4 heads x 4608 tokens), all outputs")
     _full_check(config_workload("h4"))
 
