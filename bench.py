@@ -5,13 +5,26 @@ on one MI355X.
 One step = one full pass of the path over one batch: the prologue pass
 (rotary table + K') and the attend stage (the attention kernel, plus the
 small merge kernel of the query tiles split across key ranges), i.e. one
-``mrope_attn_fwd`` call, on inputs already resident in HBM. Default workload: the 1024px shape
-(B=1, H=32, head_dim=128, 512 text + 64x64 image tokens = 4608 tokens).
+``mrope_attn_fwd`` call, on inputs already resident in HBM. Default workload:
+the 1024px shape (B=1, H=32, head_dim=128, 512 text + 64x64 image tokens =
+4608 tokens).
 
-Prints one JSON line. ``value`` is algorithmic TFLOP/s of the whole step
-(4*H*D*sum_b n_b^2 over real tokens), ``roofline`` the attend stage's own
-rate (HIP events around it on its stream) against the bf16 dense MFMA peak, and ``cpu_baseline`` the fp64 oracle timed on the host on
-the same workload (with the GPU output checked against it).
+Timing protocol. Before the counted warm-up, a declared time-based pre-warm
+runs back-to-back steps for ``--prewarm-s`` seconds (the engine clock of a
+GPU that was idle ramps up over the first few hundred milliseconds of load;
+the pre-warm and its length are reported as ``prewarm``). Then ``--warmup``
+untimed steps, then exactly ``--steps`` timed steps, each bracketed by HIP
+events on the stream the kernels run on.
+
+Prints one JSON line. ``value`` is algorithmic TFLOP/s of the whole timed
+region (4*H*D*sum_b n_b^2 over real tokens, times the steps, over the events
+around all of them); ``roofline`` is the attend stage's rate at its MEDIAN
+per-step event time against the bf16 dense MFMA peak, with min / p90 / max and
+the first- and last-quarter medians beside it; ``cpu_baseline`` is the fp64
+oracle timed on the host on the same workload (with the GPU output checked
+against it). ``extras`` carries the grouped guided step, the backward and the
+fp8 projection at the same shape, each timed after the headline region with
+its own warm-up (medians of per-call events).
 """
 
 from __future__ import annotations
@@ -30,6 +43,7 @@ METRIC = "fused QK-norm+M-RoPE attention TFLOP/s & % bf16 MFMA peak, 4608 tok"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "diffusion_transformer_image_head_amd", "csrc")
+DATA = "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights)"
 
 
 # sources the forward attention's kernels and launches are built from
@@ -44,19 +58,24 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(config: str):
-    """HBM bytes per attend stage from the committed rocprofv3 counter
-    summary (``key: value`` lines), when it was taken on the current kernel
-    sources; else None."""
-    path = os.path.join(PROFILES, f"attn_bf16_{config}_hbm_traffic.txt")
-    if not os.path.exists(path):
-        return None
+def profile_record(name: str) -> dict:
+    """``key: value`` lines of a committed rocprofv3 summary, or {}."""
+    path = os.path.join(PROFILES, name)
     rec = {}
+    if not os.path.exists(path):
+        return rec
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 rec[k.strip()] = v.strip()
+    return rec
+
+
+def traffic_from_profile(config: str):
+    """HBM bytes per attend stage from the committed rocprofv3 counter
+    summary, when it was taken on the current kernel sources; else None."""
+    rec = profile_record(f"attn_bf16_{config}_hbm_traffic.txt")
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
@@ -78,50 +97,113 @@ def calibrate_copy(nbytes: int = 256 << 20, reps: int = 5):
     print(json.dumps({"calibration": "device copy", "bytes_per_copy": nbytes, "copies": reps}), flush=True)
 
 
-def cpu_baseline(w, gpu_out):
-    """fp64 oracle on the host over the whole workload; also the parity check."""
+# ---- timing -----------------------------------------------------------------
+
+def summarize(ms) -> dict:
+    """Median, mean, min, p90, max and first/last-quarter medians (ms)."""
     import numpy as np
-    from oracle.reference import oracle_fwd
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
+    a = np.asarray(ms, dtype=np.float64)
+    q = max(1, len(a) // 4)
+    r = lambda x: round(float(x), 5)  # noqa: E731
+    return {"median": r(np.median(a)), "mean": r(a.mean()), "min": r(a.min()),
+            "p90": r(np.percentile(a, 90)), "max": r(a.max()),
+            "first_quarter_median": r(np.median(a[:q])), "last_quarter_median": r(np.median(a[-q:]))}
+
+
+def prewarm(stages, seconds: float) -> dict:
+    """Back-to-back calls for at least `seconds` of wall time (synchronising
+    every 10 calls), so the timed region does not start on an idle clock."""
+    import torch
+    if seconds <= 0:
+        return {"seconds": 0.0, "calls": 0}
     t0 = time.perf_counter()
-    ref, _ = oracle_fwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens,
-                        text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps)
-    dt = time.perf_counter() - t0
-    d = gpu_out - ref
-    rel = float(np.sqrt((d * d).sum() / (ref * ref).sum()))
-    return {
-        "value": round(w.flops() / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-        "kind": "oracle", "seconds": round(dt, 3),
-        "sample": f"the whole workload ({w.shape[2]} heads, all {w.shape[1]} query rows), fp64 NumPy",
-    }, {"max_abs": float(np.abs(d).max()), "rel_rms": rel}
+    n = 0
+    while True:
+        for _ in range(10):
+            for fn in stages:
+                fn()
+        n += 10
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return {"seconds": round(time.perf_counter() - t0, 3), "calls": n}
 
 
-def bench_cfg(args):
-    """One guided sampling step at 1024px: the conditional pass (512 text slots
-    + 64x64 image) and the unconditional pass (the 4096 image tokens alone)
-    as one grouped call, against the same two problems as two plain calls."""
+def timed_calls(stages, warmup: int, steps: int) -> dict:
+    """`warmup` untimed calls, then `steps` calls each bracketed by HIP events
+    on the current stream (the stream the binding launches on), with one more
+    event after every stage. Returns per-call totals and per-stage times (ms)
+    and the whole timed region's event time."""
+    import torch
+    for _ in range(warmup):
+        for fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, fn in enumerate(stages):
+            fn()
+            ev[i][j + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total = [e[0].elapsed_time(e[-1]) for e in ev]
+    per_stage = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(stages))]
+    return {"total": total, "stages": per_stage, "region_ms": ev[0][0].elapsed_time(end), "wall_s": wall}
+
+
+def tflops(flops: float, ms: float) -> float:
+    return flops / (ms * 1e-3) / 1e12
+
+
+# ---- the workloads ----------------------------------------------------------
+
+def to_dev(x, dtype=None):
     import numpy as np
     import torch
-    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_attn_group
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.device("cuda:0"))
+    return t if dtype is None else t.to(dtype)
+
+
+def setup_forward(config: str, kprologue: str = "auto"):
+    """(workload, [prepare, attend], out) of one plain call on a configuration."""
+    import torch
+    from diffusion_transformer_image_head_amd.binding import prepared_call
+    from diffusion_transformer_image_head_amd.workloads import config_workload
+
+    w = config_workload(config)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (w.q, w.k, w.v))
+    sl = None if w.seq_lens is None else to_dev(w.seq_lens)
+    prepare, attend, out = prepared_call(q, k, v, to_dev(w.pos), to_dev(w.gamma_q), to_dev(w.gamma_k), sl,
+                                         text_pad=w.text_pad, section=w.section, kprologue=kprologue)
+    return w, [prepare, attend], out
+
+
+def setup_cfg():
+    """One guided sampling step at 1024px: the conditional pass (512 text
+    slots + 64x64 image) and the unconditional pass (the 4096 image tokens
+    alone) as one grouped call; also the same two problems as two plain calls.
+    Returns (cond workload, flops, grouped fn, separate fn, cond out)."""
+    import numpy as np
+    import torch
+    from diffusion_transformer_image_head_amd.binding import mrope_attn, mrope_attn_group
     from diffusion_transformer_image_head_amd.workloads import config_workload, make_workload
 
-    lib()
     cond = config_workload("1024px")
     unc = make_workload(1, 32, 128, (16, 24, 24), 0, 64, 64, dtype="bf16", seed=21)
     unc.pos = np.ascontiguousarray(cond.pos[:, cond.text_pad:])
-    dev = torch.device("cuda:0")
     probs = []
     for w in (cond, unc):
-        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
-        probs.append(dict(q=t(w.q).to(torch.bfloat16), k=t(w.k).to(torch.bfloat16),
-                          v=t(w.v).to(torch.bfloat16), pos=t(w.pos), gamma_q=t(w.gamma_q),
-                          gamma_k=t(w.gamma_k), text_pad=w.text_pad, section=w.section))
+        probs.append(dict(q=to_dev(w.q, torch.bfloat16), k=to_dev(w.k, torch.bfloat16),
+                          v=to_dev(w.v, torch.bfloat16), pos=to_dev(w.pos), gamma_q=to_dev(w.gamma_q),
+                          gamma_k=to_dev(w.gamma_k), text_pad=w.text_pad, section=w.section))
     for p in probs:
         p["out"] = torch.empty_like(p["q"])
+    dev = torch.device("cuda:0")
     ws = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
     ws2 = torch.empty(1 << 27, dtype=torch.uint8, device=dev)
 
@@ -129,66 +211,56 @@ def bench_cfg(args):
         mrope_attn_group(probs, workspace=ws)
 
     def separate():
-        for p, w in zip(probs, (ws, ws2)):
+        for p, wsp in zip(probs, (ws, ws2)):
             mrope_attn(p["q"], p["k"], p["v"], p["pos"], p["gamma_q"], p["gamma_k"],
-                       text_pad=p["text_pad"], section=p["section"], out=p["out"], workspace=w)
+                       text_pad=p["text_pad"], section=p["section"], out=p["out"], workspace=wsp)
 
-    def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(args.steps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-
-    ms_sep = timed(separate)
-    ms = timed(grouped)
-    flops = cond.flops() + unc.flops()
-    value = flops / (ms * 1e-3) / 1e12
-    rec = {
-        "metric": METRIC + " (guided step: cond + uncond)", "value": round(value, 3),
-        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights)",
-        "config": {"workload": "cfg1024: 1024px cond (B=1 H=32 D=128, 512 text + 64x64 image) "
-                               "+ image-only uncond (4096 tokens), one grouped call"},
-        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "whole grouped call (prologues + attention + merge)"},
-        "separate_calls": {"ms_per_step": round(ms_sep, 5),
-                           "value": round(flops / (ms_sep * 1e-3) / 1e12, 3)},
-    }
-    if not args.no_cpu_baseline:
-        base, par = cpu_baseline(cond, probs[0]["out"].float().cpu().numpy().astype(np.float64))
-        rec["cpu_baseline"] = dict(base, sample="the conditional pass only (" + base["sample"] + ")")
-        rec["parity"] = par
-    print(json.dumps(rec), flush=True)
+    return cond, cond.flops() + unc.flops(), grouped, separate, probs[0]["out"]
 
 
-def bench_qkv(args):
-    """The layer's attention input path at a configuration's shape: x [B*S,
-    hidden = H*D] bf16 through the fp8 e4m3 fused qkv weight with the
-    norm/rotation epilogue (one call), then the attention on those operands.
-    value = the projection's FLOP rate (2 * tokens * hidden * 3 H D)."""
+def setup_bwd(config: str):
+    """The backward pass on a configuration: one untimed forward for out and
+    lse, then a callable running one backward. FLOPs: the usual 2.5x the
+    forward's (dV, dP, dQ, dK and the recomputed S: five S^2 D products
+    against the forward's two)."""
     import numpy as np
     import torch
-    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_qkv_proj
+    from diffusion_transformer_image_head_amd.binding import mrope_attn, mrope_attn_bwd
+    from diffusion_transformer_image_head_amd.workloads import config_workload, round_to_bf16
+
+    w = config_workload(config)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (w.q, w.k, w.v))
+    pos, gq, gk = to_dev(w.pos), to_dev(w.gamma_q), to_dev(w.gamma_k)
+    sl = None if w.seq_lens is None else to_dev(w.seq_lens)
+    kw = dict(text_pad=w.text_pad, section=w.section)
+    out, lse = mrope_attn(q, k, v, pos, gq, gk, sl, return_lse=True, **kw)
+    do = to_dev(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32)),
+                torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=torch.device("cuda:0"))
+
+    def step():
+        mrope_attn_bwd(q, k, v, pos, gq, gk, sl, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+
+    return w, 2.5 * w.flops(), step
+
+
+def setup_qkv(config: str):
+    """The layer's attention input path at a configuration's shape: x [B*S,
+    hidden = H*D] bf16 through the fp8 e4m3 fused qkv weight with the
+    norm/rotation epilogue (one call), and the attention on those operands.
+    Returns (workload, projection flops, proj fn, attend fn, attention flops)."""
+    import torch
+    from diffusion_transformer_image_head_amd.binding import mrope_attn, mrope_qkv_proj
     from diffusion_transformer_image_head_amd.workloads import CONFIGS, make_qkv_workload
 
-    lib()
-    c = CONFIGS[args.config]
+    c = CONFIGS[config]
     h, d = c["heads"], c["head_dim"]
     w = make_qkv_workload(c["batch"], h, d, c["section"], c["text_pad"], c["grid_h"], c["grid_w"],
                           h * d, seed=c["seed"])
     dev = torch.device("cuda:0")
-    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    x = t(w.x).to(torch.bfloat16)
-    w8, wsc, pos, gq, gk = t(w.w8), t(w.w_scale), t(w.pos), t(w.gamma_q), t(w.gamma_k)
+    x = to_dev(w.x, torch.bfloat16)
+    w8, wsc, pos, gq, gk = to_dev(w.w8), to_dev(w.w_scale), to_dev(w.pos), to_dev(w.gamma_q), to_dev(w.gamma_k)
     outs = tuple(torch.empty((w.x.shape[0], h, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
     ws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
     b, s = w.batch, w.seq
@@ -203,121 +275,161 @@ def bench_qkv(args):
         mrope_attn(q, k, v, None, None, None, text_pad=w.text_pad, kprologue="none", out=att_out,
                    workspace=att_ws)
 
-    def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+    return w, w.flops(), proj, attend, 4 * h * d * s * s * b
 
-    ms_p = timed(proj)
-    ms_a = timed(attend)
-    value = w.flops() / (ms_p * 1e-3) / 1e12
-    att_flops = 4 * h * d * s * s * b
-    rec = {
-        "metric": "fp8 QKV projection + norm/rotation epilogue TFLOP/s (bf16 matrix cores)",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_p, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) x, N(0,1/hidden) weight quantized to e4m3 per row)",
-        "config": {"workload": f"{args.config} qkv: tokens={b * s} hidden={h * d} out={3 * h * d}"},
-        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "rope_table_kernel + qkv_proj_kernel"},
-        "attention_on_operands": {"ms": round(ms_a, 5),
-                                  "TFLOP/s": round(att_flops / (ms_a * 1e-3) / 1e12, 3)},
-    }
+
+# ---- oracle baseline --------------------------------------------------------
+
+def host_threads() -> dict:
+    """os.cpu_count(), the affinity count and the BLAS thread count."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = None
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = None
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": blas}
+
+
+def cpu_baseline(w, gpu_out, runs: int):
+    """The fp64 oracle on the host over the whole workload, `runs` times
+    (median reported); also the parity check of the GPU output."""
+    import numpy as np
+    from oracle.reference import oracle_fwd
+    secs = []
+    ref = None
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        ref, _ = oracle_fwd(w.q, w.k, w.v, w.pos, w.gamma_q, w.gamma_k, w.seq_lens,
+                            text_pad=w.text_pad, section=w.section, theta=w.theta, eps=w.eps)
+        secs.append(time.perf_counter() - t0)
+    dt = float(np.median(secs))
+    d = gpu_out - ref
+    rel = float(np.sqrt((d * d).sum() / (ref * ref).sum()))
+    th = host_threads()
+    return {
+        "value": round(w.flops() / dt / 1e12, 6), "unit": "TFLOP/s",
+        # matmuls run on the BLAS pool, the elementwise steps on one thread
+        "cores": int(th["blas_threads"] or th["affinity"] or th["cpu_count"]),
+        "kind": "oracle", "seconds": round(dt, 3), "runs": [round(s, 3) for s in secs], **th,
+        "sample": f"the whole workload ({w.shape[2]} heads, all {w.shape[1]} query rows), fp64 NumPy, "
+                  f"median of {runs} runs",
+    }, {"max_abs": float(np.abs(d).max()), "rel_rms": rel}
+
+
+# ---- sub-benchmarks ---------------------------------------------------------
+
+def base_record(args, metric, value, ms, workload, dtype="bf16"):
+    return {"metric": metric, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": DATA, "config": {"workload": workload}}
+
+
+def roofline(achieved, kernel, **kw):
+    return dict({"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": kernel}, **kw)
+
+
+def bench_cfg(args):
+    """cfg1024: one guided step (cond + uncond) as one grouped call, against
+    the same two problems as two plain calls."""
+    import numpy as np
+    cond, flops, grouped, separate, out = setup_cfg()
+    pw = prewarm([grouped], args.prewarm_s)
+    sep = timed_calls([separate], args.warmup, args.steps)
+    grp = timed_calls([grouped], args.warmup, args.steps)
+    ms = grp["region_ms"] / args.steps
+    med = float(np.median(grp["total"]))
+    rec = base_record(args, METRIC + " (guided step: cond + uncond)", tflops(flops, ms), ms,
+                      "cfg1024: 1024px cond (B=1 H=32 D=128, 512 text + 64x64 image) "
+                      "+ image-only uncond (4096 tokens), one grouped call")
+    rec["roofline"] = roofline(tflops(flops, med), "whole grouped call (prologues + attention + merge)",
+                               kernel_ms=round(med, 5))
+    rec["prewarm"] = pw
+    rec["call_ms"] = summarize(grp["total"])
+    rec["separate_calls"] = {"ms_median": round(float(np.median(sep["total"])), 5),
+                             "value": round(tflops(flops, float(np.median(sep["total"]))), 3)}
+    if not args.no_cpu_baseline:
+        base, par = cpu_baseline(cond, out.float().cpu().numpy().astype(np.float64), 1)
+        rec["cpu_baseline"] = dict(base, sample="the conditional pass only (" + base["sample"] + ")")
+        rec["parity"] = par
+    print(json.dumps(rec), flush=True)
+
+
+def bench_qkv(args):
+    """fp8 QKV projection with the norm/rotation epilogue, then the attention
+    on its operands. value = the projection's FLOP rate (2 * tokens * hidden
+    * 3 H D)."""
+    import numpy as np
+    w, flops, proj, attend, att_flops = setup_qkv(args.config)
+    pw = prewarm([proj], args.prewarm_s)
+    tp = timed_calls([proj], args.warmup, args.steps)
+    ta = timed_calls([attend], args.warmup, args.steps)
+    ms = tp["region_ms"] / args.steps
+    med = float(np.median(tp["total"]))
+    rec = base_record(args, "fp8 QKV projection + norm/rotation epilogue TFLOP/s (bf16 matrix cores)",
+                      tflops(flops, ms), ms,
+                      f"{args.config} qkv: tokens={w.batch * w.seq} hidden={w.heads * w.head_dim} "
+                      f"out={3 * w.heads * w.head_dim}")
+    rec["data"] = "synthetic (seeded N(0,1) x, N(0,1/hidden) weight quantized to e4m3 per row)"
+    rec["roofline"] = roofline(tflops(flops, med), "rope_table_kernel + qkv_proj_kernel", kernel_ms=round(med, 5))
+    rec["prewarm"] = pw
+    rec["call_ms"] = summarize(tp["total"])
+    am = float(np.median(ta["total"]))
+    rec["attention_on_operands"] = {"ms_median": round(am, 5), "TFLOP/s": round(tflops(att_flops, am), 3)}
     print(json.dumps(rec), flush=True)
 
 
 def bench_bwd(args):
-    """Backward pass on a configuration: the forward runs once (untimed) for
-    out and lse, then `steps` backward calls are timed. FLOPs: the usual 2.5x
-    the forward's (dV, dP, dQ, dK and the recomputed S: five S^2 D products
-    against the forward's two)."""
+    """Backward pass on a configuration (2.5x the forward's FLOPs)."""
     import numpy as np
-    import torch
-    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn, mrope_attn_bwd
-    from diffusion_transformer_image_head_amd.workloads import config_workload, round_to_bf16
-
-    lib()
-    w = config_workload(args.config)
-    dev = torch.device("cuda:0")
-    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
-    q, k, v = (t(x).to(torch.bfloat16) for x in (w.q, w.k, w.v))
-    pos, gq, gk = t(w.pos), t(w.gamma_q), t(w.gamma_k)
-    sl = None if w.seq_lens is None else t(w.seq_lens)
-    kw = dict(text_pad=w.text_pad, section=w.section)
-    out, lse = mrope_attn(q, k, v, pos, gq, gk, sl, return_lse=True, **kw)
-    do = t(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32))).to(torch.bfloat16)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
-
-    def step():
-        mrope_attn_bwd(q, k, v, pos, gq, gk, sl, out, lse, do, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(args.steps):
-        step()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / args.steps
-    flops = 2.5 * w.flops()
-    value = flops / (ms * 1e-3) / 1e12
+    w, flops, step = setup_bwd(args.config)
+    pw = prewarm([step], args.prewarm_s)
+    tb = timed_calls([step], args.warmup, args.steps)
+    ms = tb["region_ms"] / args.steps
+    med = float(np.median(tb["total"]))
     bb, s, h, d = w.shape
-    rec = {
-        "metric": "fused QK-norm+M-RoPE attention backward TFLOP/s (2.5x forward FLOPs)",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q/k/v/dO, U[0.5,1.5) gammas; no dataset or weights)",
-        "config": {"workload": f"{args.config} backward: B={bb} H={h} head_dim={d} tokens={s}"},
-        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "whole backward call (prologues, delta, dk/dv, dq, dgamma)"},
-    }
+    rec = base_record(args, "fused QK-norm+M-RoPE attention backward TFLOP/s (2.5x forward FLOPs)",
+                      tflops(flops, ms), ms, f"{args.config} backward: B={bb} H={h} head_dim={d} tokens={s}")
+    rec["data"] = DATA.replace("q/k/v", "q/k/v/dO")
+    rec["roofline"] = roofline(tflops(flops, med), "whole backward call (prologues, delta, dk/dv/dq, dgamma)",
+                               kernel_ms=round(med, 5))
+    rec["prewarm"] = pw
+    rec["call_ms"] = summarize(tb["total"])
     print(json.dumps(rec), flush=True)
 
 
 def bench_packed(args):
     """A configuration's prompts packed back to back (cu_seqlens; each
     prompt's true-length text tokens then its image) instead of padded:
-    `steps` calls of the packed forward (prologue + attention), or with
-    --backward of the packed backward after one untimed forward. FLOPs are the
-    sequences' own: 4 H D sum(n_b^2), times 2.5 for the backward."""
+    the packed forward (prologue + attention), or with --backward the packed
+    backward after one untimed forward. FLOPs are the sequences' own: 4 H D
+    sum(n_b^2), times 2.5 for the backward."""
     import numpy as np
     import torch
-    from diffusion_transformer_image_head_amd.binding import lib, mrope_attn_bwd_varlen, mrope_attn_varlen
+    from diffusion_transformer_image_head_amd.binding import mrope_attn_bwd_varlen, mrope_attn_varlen
     from diffusion_transformer_image_head_amd.workloads import CONFIGS, make_varlen_workload, round_to_bf16
 
-    lib()
     c = CONFIGS[args.config]
     lens = c["text_lens"] if c["text_lens"] is not None else (c["text_pad"],) * c["batch"]
     w = make_varlen_workload(c["heads"], c["head_dim"], c["section"], text_lens=lens,
                              grids=[(c["grid_h"], c["grid_w"])] * c["batch"], sigma=c["sigma"],
                              seed=c["seed"])
-    dev = torch.device("cuda:0")
-    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
-    q, k, v = (t(x).to(torch.bfloat16) for x in (w.q, w.k, w.v))
-    pos, gq, gk = t(w.pos), t(w.gamma_q), t(w.gamma_k)
-    cu = t(w.cu_seqlens.astype(np.int32))
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (w.q, w.k, w.v))
+    pos, gq, gk = to_dev(w.pos), to_dev(w.gamma_q), to_dev(w.gamma_k)
+    cu = to_dev(w.cu_seqlens.astype(np.int32))
     ms_len = w.max_seqlen
     out = torch.empty_like(q)
-    ws = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    ws = torch.empty(1 << 29, dtype=torch.uint8, device=torch.device("cuda:0"))
     _, lse = mrope_attn_varlen(q, k, v, pos, gq, gk, cu, ms_len, section=w.section, return_lse=True,
                                out=out, workspace=ws)
     if args.backward:
-        do = t(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32)))
-        do = do.to(torch.bfloat16)
+        do = to_dev(round_to_bf16(np.random.default_rng(3).standard_normal(w.q.shape).astype(np.float32)),
+                    torch.bfloat16)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
         def step():
@@ -327,33 +439,94 @@ def bench_packed(args):
         def step():
             mrope_attn_varlen(q, k, v, pos, gq, gk, cu, ms_len, section=w.section, out=out, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    pw = prewarm([step], args.prewarm_s)
+    tm = timed_calls([step], args.warmup, args.steps)
+    ms = tm["region_ms"] / args.steps
+    med = float(np.median(tm["total"]))
     mult = 2.5 if args.backward else 1.0
-    value = mult * w.flops() / (ms * 1e-3) / 1e12
     what = "backward" if args.backward else "forward"
-    rec = {
-        "metric": f"fused QK-norm+M-RoPE attention {what} TFLOP/s, packed sequences"
-                  + (" (2.5x forward FLOPs)" if args.backward else ""),
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q/k/v/dO, U[0.5,1.5) gammas; no dataset or weights)",
-        "config": {"workload": f"{args.config} packed {what}: {len(lens)} sequences, "
-                               f"{w.q.shape[0]} tokens, H={c['heads']} head_dim={c['head_dim']}",
-                   "cu_seqlens": [int(x) for x in w.cu_seqlens]},
-        "roofline": {"bound": "mfma", "achieved": round(value, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(value / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": f"whole packed {what} call"},
-    }
+    rec = base_record(args, f"fused QK-norm+M-RoPE attention {what} TFLOP/s, packed sequences"
+                      + (" (2.5x forward FLOPs)" if args.backward else ""), tflops(mult * w.flops(), ms), ms,
+                      f"{args.config} packed {what}: {len(lens)} sequences, {w.q.shape[0]} tokens, "
+                      f"H={c['heads']} head_dim={c['head_dim']}")
+    rec["config"]["cu_seqlens"] = [int(x) for x in w.cu_seqlens]
+    rec["roofline"] = roofline(tflops(mult * w.flops(), med), f"whole packed {what} call", kernel_ms=round(med, 5))
+    rec["prewarm"] = pw
+    rec["call_ms"] = summarize(tm["total"])
+    print(json.dumps(rec), flush=True)
+
+
+def extras(args) -> dict:
+    """The grouped guided step, the backward and the fp8 projection at the
+    1024px shape, each after its own warm-up; medians of per-call events."""
+    import numpy as np
+    import torch
+    res = {}
+    warm, steps = max(args.warmup, 10), max(args.steps, 20)
+    _, flops, grouped, _, _ = setup_cfg()
+    g = timed_calls([grouped], warm, steps)
+    gm = float(np.median(g["total"]))
+    res["cfg1024_grouped"] = {"ms_median": round(gm, 5), "TFLOP/s": round(tflops(flops, gm), 3),
+                              "what": "cond 4608 + image-only uncond 4096 tokens, H=32, one grouped call"}
+    torch.cuda.empty_cache()
+    _, flops, step = setup_bwd("1024px")
+    b = timed_calls([step], warm, steps)
+    bm = float(np.median(b["total"]))
+    res["backward_1024px"] = {"ms_median": round(bm, 5), "TFLOP/s": round(tflops(flops, bm), 3),
+                              "what": "dq, dk, dv, dgammas; FLOPs 2.5x the forward's"}
+    torch.cuda.empty_cache()
+    _, flops, proj, _, _ = setup_qkv("1024px")
+    p = timed_calls([proj], warm, steps)
+    pm = float(np.median(p["total"]))
+    res["qkv_proj_1024px"] = {"ms_median": round(pm, 5), "TFLOP/s": round(tflops(flops, pm), 3),
+                              "what": "x [4608, 4096] bf16 x fp8 e4m3 W [12288, 4096] with row scales, "
+                                      "norm/rotation epilogue"}
+    for r in res.values():
+        r["frac"] = round(r["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
+    res["protocol"] = f"{warm} warm-up + {steps} timed calls each, after the headline region"
+    return res
+
+
+def bench_forward(args):
+    import numpy as np
+    from diffusion_transformer_image_head_amd.binding import lib
+
+    lib()  # fail loudly without the HIP library
+    w, stages, out = setup_forward(args.config, args.kprologue)
+    b, s, h, d = w.shape
+    pw = prewarm(stages, args.prewarm_s)
+    tm = timed_calls(stages, args.warmup, args.steps)
+    flops = w.flops()
+    ms_step = tm["region_ms"] / args.steps
+    att = tm["stages"][1]
+    att_med = float(np.median(att))
+    value = tflops(flops, ms_step)
+    achieved = tflops(flops, att_med)
+    rec = base_record(args, METRIC, value, ms_step,
+                      f"{args.config}: B={b} H={h} head_dim={d} tokens={s} "
+                      f"(text_pad={w.text_pad} + {w.grid[0]}x{w.grid[1]} image)")
+    rec["config"].update({"batch": b, "heads": h, "head_dim": d, "seq_len": s, "section": list(w.section),
+                          "kprologue": args.kprologue,
+                          "text_lens": None if w.seq_lens is None else [int(x) for x in w.seq_lens]})
+    rec["roofline"] = roofline(achieved, "attn_bf16_kernel + split_merge_kernel (attend stage)",
+                               traffic=traffic_from_profile(args.config), kernel_ms=round(att_med, 5),
+                               statistic="median of per-step HIP events around the attend stage")
+    rec["attend_ms"] = summarize(att)
+    rec["step_ms"] = summarize(tm["total"])
+    rec["prologue_ms_median"] = round(float(np.median(tm["stages"][0])), 5)
+    rec["frac_of_peak_whole_step"] = round(value / PEAK_BF16_TFLOPS, 4)
+    rec["prewarm"] = pw
+    rec["wall_s"] = round(tm["wall_s"], 4)
+    rec["kernel_source_hash"] = kernel_source_hash()
+    if not args.no_extras and args.config == "1024px":
+        rec["extras"] = extras(args)
+    if not args.no_cpu_baseline:
+        got = out.float().cpu().numpy().astype(np.float64)
+        runs = 3 if s <= 4608 and b == 1 else 1
+        base, parity = cpu_baseline(w, got, runs)
+        rec["cpu_baseline"] = base
+        rec["parity"] = dict(parity, bars={"max_abs": 2e-2, "rel_rms": 5e-3},
+                             ok=bool(parity["max_abs"] <= 2e-2 and parity["rel_rms"] <= 5e-3))
     print(json.dumps(rec), flush=True)
 
 
@@ -362,12 +535,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of back-to-back untimed steps before the counted warm-up (declared "
+                         "in the output; the clock of an idle GPU ramps up under load)")
     ap.add_argument("--config", default="1024px",
                     choices=["512px", "1024px", "ragged", "long", "h36", "2048px", "cfg1024", "h4"],
                     help="cfg1024: one guided step, the 1024px conditional pass and its "
                          "image-only unconditional pass in one grouped call")
     ap.add_argument("--kprologue", default="auto", choices=["auto", "prepass", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the grouped-step / backward / projection timings of the default line")
     ap.add_argument("--qkv", action="store_true",
                     help="time the fp8 QKV projection with the norm/rotation epilogue, then the "
                          "attention on its operands (kprologue none)")
@@ -386,91 +564,22 @@ def main():
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               "(heads/batch shard with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
+    from diffusion_transformer_image_head_amd.binding import lib
+    lib()  # fail loudly without the HIP library
     if args.config == "cfg1024":
         bench_cfg(args)
-        return
-    if args.packed:
+    elif args.packed:
         bench_packed(args)
-        return
-    if args.backward:
+    elif args.backward:
         bench_bwd(args)
-        return
-    if args.qkv:
+    elif args.qkv:
         bench_qkv(args)
-        return
-
-    import numpy as np
-    import torch
-    from diffusion_transformer_image_head_amd.binding import lib, prepared_call
-    from diffusion_transformer_image_head_amd.workloads import config_workload
-
-    lib()  # fail loudly without the HIP library
-    dev = torch.device("cuda:0")
-    w = config_workload(args.config)
-    b, s, h, d = w.shape
-    q = torch.from_numpy(w.q).to(dev).to(torch.bfloat16)
-    k = torch.from_numpy(w.k).to(dev).to(torch.bfloat16)
-    v = torch.from_numpy(w.v).to(dev).to(torch.bfloat16)
-    pos = torch.from_numpy(w.pos).to(dev)
-    gq = torch.from_numpy(w.gamma_q).to(dev)
-    gk = torch.from_numpy(w.gamma_k).to(dev)
-    sl = None if w.seq_lens is None else torch.from_numpy(w.seq_lens).to(dev)
-    prepare, attend, out = prepared_call(q, k, v, pos, gq, gk, sl, text_pad=w.text_pad,
-                                         section=w.section, kprologue=args.kprologue)
-
-    for _ in range(args.warmup):
-        prepare()
-        attend()
-    torch.cuda.synchronize()
-
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        prepare()
-        mids[i].record()
-        attend()
-        ends[i].record()
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    attn_ms = float(np.mean([m.elapsed_time(e) for m, e in zip(mids, ends)]))
-
-    flops = w.flops()
-    ms_step = total_ms / args.steps
-    value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    rec = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights)",
-        "config": {"workload": f"{args.config}: B={b} H={h} head_dim={d} tokens={s} "
-                               f"(text_pad={w.text_pad} + {w.grid[0]}x{w.grid[1]} image)",
-                   "batch": b, "heads": h, "head_dim": d, "seq_len": s,
-                   "section": list(w.section), "kprologue": args.kprologue,
-                   "text_lens": None if w.seq_lens is None else [int(x) for x in w.seq_lens]},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(args.config),
-                     "kernel_ms": round(attn_ms, 5), "kernel": "attn_bf16_kernel + split_merge_kernel"},
-        "frac_of_peak_whole_step": round(value / PEAK_BF16_TFLOPS, 4),
-        "wall_s": round(wall, 4),
-        "kernel_source_hash": kernel_source_hash(),
-    }
-    if not args.no_cpu_baseline:
-        got = out.float().cpu().numpy().astype(np.float64)
-        base, parity = cpu_baseline(w, got)
-        rec["cpu_baseline"] = base
-        rec["parity"] = dict(parity, bars={"max_abs": 2e-2, "rel_rms": 5e-3},
-                             ok=bool(parity["max_abs"] <= 2e-2 and parity["rel_rms"] <= 5e-3))
-    print(json.dumps(rec), flush=True)
+    else:
+        bench_forward(args)
 
 
 if __name__ == "__main__":

@@ -86,6 +86,11 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m diffusion_transformer_image_head_amd.build`")
+        # torch ships its own HIP runtime under the same soname
+        # (libamdhip64.so.7). Importing torch first makes the library bind to
+        # that one instance: a second runtime loaded beside it sees no device,
+        # and torch's stream handles belong to torch's runtime.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp, i32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         L.mrope_attn_validate.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp]
@@ -101,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_attend.restype = ctypes.c_int
         L.mrope_attn_status_string.argtypes = [ctypes.c_int]
         L.mrope_attn_status_string.restype = ctypes.c_char_p
+        L.mrope_attn_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
+        L.mrope_attn_last_hip_error.restype = ctypes.c_int
         L.mrope_attn_group_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int]
         L.mrope_attn_group_workspace_size.restype = ctypes.c_size_t
         L.mrope_attn_fwd_group.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Problem), ctypes.c_int,
@@ -135,6 +142,21 @@ def lib() -> ctypes.CDLL:
 
 def status_string(status: int) -> str:
     return lib().mrope_attn_status_string(status).decode()
+
+
+def last_hip_error():
+    """(hipError_t, name) behind this thread's most recent MRA_ERR_HIP."""
+    name = ctypes.c_char_p()
+    code = lib().mrope_attn_last_hip_error(ctypes.byref(name))
+    return int(code), (name.value or b"").decode()
+
+
+def _error(rc: int) -> MraError:
+    msg = status_string(rc)
+    if rc == -8:
+        code, name = last_hip_error()
+        msg += f" (hipError_t {code}: {name})"
+    return MraError(rc, msg)
 
 
 def make_desc(batch, seq, heads, head_dim, *, text_pad, section=(16, 24, 24), theta=10000.0,
@@ -257,7 +279,7 @@ def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     else:
         raise ValueError(f"unknown stage {stage}")
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return (out, lse) if return_lse else out
 
 
@@ -325,7 +347,7 @@ def mrope_attn_group(problems, *, return_lse: bool = False, kprologue="auto", wo
     rc = lib().mrope_attn_fwd_group(darr, parr, n, None if not need else workspace.data_ptr(),
                                     need, stream)
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return results
 
 
@@ -365,7 +387,7 @@ def mrope_attn_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen: in
                                      None if lse is None else lse.data_ptr(),
                                      None if not need else workspace.data_ptr(), need, stream)
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return (out, lse) if return_lse else out
 
 
@@ -405,7 +427,7 @@ def mrope_attn_bwd(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, lse, dout, *, 
                               dv.data_ptr(), dgq.data_ptr(), dgk.data_ptr(),
                               None if not need else workspace.data_ptr(), need, stream)
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return dq, dk, dv, dgq, dgk
 
 
@@ -452,7 +474,7 @@ def mrope_attn_bwd_varlen(q, k, v, pos, gamma_q, gamma_k, cu_seqlens, max_seqlen
                                      dv.data_ptr(), dgq.data_ptr(), dgk.data_ptr(),
                                      None if not need else workspace.data_ptr(), need, stream)
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return dq, dk, dv, dgq, dgk
 
 
@@ -517,5 +539,5 @@ def mrope_qkv_proj(x, w8, w_scale, pos, gamma_q, gamma_k, *, heads: int, section
                               out[1].data_ptr(), out[2].data_ptr(),
                               None if not need else workspace.data_ptr(), need, stream)
     if rc != 0:
-        raise MraError(rc, status_string(rc))
+        raise _error(rc)
     return out

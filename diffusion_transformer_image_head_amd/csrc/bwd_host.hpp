@@ -130,7 +130,7 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
                        (const float*)g.dgq_part, (const float*)g.dgk_part, n, run, stride, dgamma_q,
                        dgamma_k);
   }
-  return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(hipGetLastError());
 }
 
 size_t mrope_attn_bwd_workspace_size(const mra_desc* d) {
@@ -154,6 +154,7 @@ int mrope_attn_bwd(const mra_desc* d, const void* q, const void* k, const void* 
   if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
   return bwd_run(d, d->batch, d->seq, seq_lens, nullptr, q, k, v, pos, gq, gk, out, lse, dout, dq, dk, dv,
                  dgamma_q, dgamma_k, workspace, (hipStream_t)stream);
 }
@@ -187,6 +188,7 @@ int mrope_attn_bwd_varlen(const mra_desc* d, const void* q, const void* k, const
   if (!workspace || ws_bytes < p.bytes || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
   return bwd_run(&lay, d->batch, max_seqlen, nullptr, cu_seqlens, q, k, v, pos, gq, gk, out, lse, dout, dq,
                  dk, dv, dgamma_q, dgamma_k, workspace, (hipStream_t)stream);
 }

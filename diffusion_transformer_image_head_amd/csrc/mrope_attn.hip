@@ -44,6 +44,21 @@ constexpr int resident_slots(int w) { return kComputeUnits * (w * kRowBlocks >= 
 #endif
 constexpr int kSplitTarget = MRA_SPLIT_TARGET;
 
+// hipError_t behind the calling thread's most recent MRA_ERR_HIP
+// (mrope_attn_last_hip_error), 0 if none yet.
+thread_local int t_last_hip_error = 0;
+
+// Takes the calling thread's pending HIP error (left by whatever ran before
+// this call) off, so that the check after this call's launches sees only
+// their own errors.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MRA_OK;
+  t_last_hip_error = (int)e;
+  return MRA_ERR_HIP;
+}
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -288,7 +303,12 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 106; }
+int mrope_attn_abi_version(void) { return 107; }
+
+int mrope_attn_last_hip_error(const char** name) {
+  if (name) *name = t_last_hip_error ? hipGetErrorName((hipError_t)t_last_hip_error) : "none";
+  return t_last_hip_error;
+}
 
 const char* mrope_attn_status_string(int status) {
   switch (status) {
@@ -355,6 +375,7 @@ static int prepare_call(const mra_desc* d, const void* q, const void* k, const v
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
   fill_args(a, d, q, k, v, pos, gq, gk, seq_lens, out, lse);
   if (d->dtype == MRA_BF16) {
     plan = make_plan(&d, 1);
@@ -374,7 +395,7 @@ int mrope_attn_prepare(const mra_desc* d, const void* k, const int32_t* pos, con
   hipStream_t s = (hipStream_t)stream;
   const int kpro = resolve_kprologue(d);
   hipError_t e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
-  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(e);
 }
 
 int mrope_attn_attend(const mra_desc* d, const void* q, const void* k, const void* v,
@@ -391,7 +412,7 @@ int mrope_attn_attend(const mra_desc* d, const void* q, const void* k, const voi
     e = d->head_dim == 128 ? launch_fp32<128>(a, s, a.S) : launch_fp32<64>(a, s, a.S);
   else
     e = launch_attend(&a, plan, workspace, d->head_dim, resolve_kprologue(d), s);
-  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(e);
 }
 
 int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* v,
@@ -411,7 +432,7 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
     e = d->head_dim == 128 ? launch_prologue_bf16<128>(a, kpro, s) : launch_prologue_bf16<64>(a, kpro, s);
     if (e == hipSuccess) e = launch_attend(&a, plan, workspace, d->head_dim, kpro, s);
   }
-  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(e);
 }
 
 // Problems of a group call that hold at least one token, in call order;
@@ -456,6 +477,7 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
   hipStream_t s = (hipStream_t)stream;
   Args as[MRA_MAX_GROUP];
   const mra_desc* ds[MRA_MAX_GROUP];
@@ -469,7 +491,7 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
   if (descs[0].dtype == MRA_FP32) {
     for (int j = 0; j < m && e == hipSuccess; ++j)
       e = D == 128 ? launch_fp32<128>(as[j], s, as[j].S) : launch_fp32<64>(as[j], s, as[j].S);
-    return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+    return hip_status(e);
   }
   const Plan plan = make_plan(ds, m);
   const int kpro = resolve_kprologue(ds[0]);
@@ -478,7 +500,7 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
     e = D == 128 ? launch_prologue_bf16<128>(as[j], kpro, s) : launch_prologue_bf16<64>(as[j], kpro, s);
   }
   if (e == hipSuccess) e = launch_attend(as, plan, workspace, D, kpro, s);
-  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(e);
 }
 
 // ---- packed variable-length sequences (cu_seqlens) ------------------------
@@ -520,6 +542,7 @@ int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
   Args a;
   fill_args(a, &lay, q, k, v, pos, gq, gk, nullptr, out, lse);
   hipStream_t s = (hipStream_t)stream;
@@ -542,7 +565,7 @@ int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const
       e = launch_attend(&a, plan, workspace, d->head_dim, kpro, s);
     }
   }
-  return e == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(e);
 }
 
 }  // extern "C"

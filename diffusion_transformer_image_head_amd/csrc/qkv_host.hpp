@@ -49,6 +49,7 @@ int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, cons
   if (!workspace || ws_bytes < need || !aligned(workspace, 16)) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
+  clear_stale_hip_error();
 
   // the rotary table of the tokens, from the same kernel the attention uses
   Args a;
@@ -92,7 +93,7 @@ int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, cons
   g.n_mt = (d->tokens + kTok - 1) / kTok;
   hipLaunchKernelGGL((mra::qkv_proj_kernel<128, kWaves, MRA_QKV_KB, MRA_QKV_NST, MRA_QKV_TPW>),
                      dim3((unsigned)(g.n_mt * head_pairs)), dim3(64 * kWaves), 0, s, g);
-  return hipGetLastError() == hipSuccess ? MRA_OK : MRA_ERR_HIP;
+  return hip_status(hipGetLastError());
 }
 
 }  // extern "C"

@@ -49,7 +49,8 @@
  *    asynchronous; results are valid after the stream synchronises.
  *  - Errors are negative mra_status values. Every contract check runs on the
  *    host before any device work; on error nothing is launched or written.
- *  - Calls are thread-safe; the library holds no global state.
+ *  - Calls are thread-safe; the library holds no global state besides the
+ *    per-thread record behind mrope_attn_last_hip_error.
  */
 #ifndef MROPE_ATTN_H
 #define MROPE_ATTN_H
@@ -300,6 +301,13 @@ int mrope_qkv_proj(const mra_qkv_desc* desc, const void* x, const uint8_t* w8, c
 
 /* Static, human-readable text for a status code. */
 const char* mrope_attn_status_string(int status);
+
+/* The hipError_t behind the calling thread's most recent MRA_ERR_HIP (0 when
+ * this thread has had none), and in *name (when name is not NULL) HIP's
+ * static name for it. Each call clears a HIP error still pending on its
+ * thread from earlier, unrelated work before its own launches, so the value
+ * is the call's own. */
+int mrope_attn_last_hip_error(const char** name);
 
 /* ABI version of this header (major * 100 + minor). */
 int mrope_attn_abi_version(void);

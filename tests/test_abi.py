@@ -10,6 +10,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -41,7 +42,8 @@ def test_header_declares_the_entry_points():
         "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_bwd",
         "mrope_attn_bwd_varlen", "mrope_attn_bwd_varlen_workspace_size",
         "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
-        "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size", "mrope_attn_prepare",
+        "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size",
+        "mrope_attn_last_hip_error", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
         "mrope_attn_workspace_size", "mrope_qkv_proj", "mrope_qkv_proj_workspace_size"])
 
@@ -68,6 +70,22 @@ def _c_layout(tmp_path, struct, fields):
     return [int(x) for x in out]
 
 
+def test_one_hip_runtime_in_the_process():
+    # torch bundles a HIP runtime with the soname of the system one; loading
+    # the library before torch would map both, and the second finds no
+    # device. The binding imports torch first, so a fresh process that only
+    # loads the library maps exactly one of each runtime library.
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from diffusion_transformer_image_head_amd import binding\n"
+            "binding.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "for key in ('libamdhip64', 'libhsa-runtime64'):\n"
+            "    print(key, len(set(l.split()[-1] for l in maps if key in l)))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True).stdout
+    assert "libamdhip64 1" in out and "libhsa-runtime64 1" in out, out
+
+
 @pytest.mark.parametrize("cls,struct", [(B.Desc, "mra_desc"), (B.QkvDesc, "mra_qkv_desc"),
                                         (B.Problem, "mra_problem")])
 def test_struct_layouts_match_header(tmp_path, cls, struct):
@@ -79,7 +97,7 @@ def test_struct_layouts_match_header(tmp_path, cls, struct):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 106
+    assert lib.mrope_attn_abi_version() == 107
     for st in range(0, -10, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
@@ -223,6 +241,11 @@ def test_fwd_rejects_before_launch(lib, monkeypatch):
     assert L.mrope_attn_prepare(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, None) == -8
     assert L.mrope_attn_attend(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                None, FAKE, need, None) == -8
+
+
+def test_last_hip_error_starts_clear(lib):
+    # no HIP error has happened on this thread (nothing here reaches the device)
+    assert B.last_hip_error() == (0, "none")
 
 
 def test_stages_validate_like_fwd(lib):
