@@ -108,6 +108,9 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_status_string.restype = ctypes.c_char_p
         L.mrope_attn_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
         L.mrope_attn_last_hip_error.restype = ctypes.c_int
+        L.mrope_attn_fwd_noalloc.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp,
+                                             f32p, vp]
+        L.mrope_attn_fwd_noalloc.restype = ctypes.c_int
         L.mrope_attn_group_workspace_size.argtypes = [ctypes.POINTER(Desc), ctypes.c_int]
         L.mrope_attn_group_workspace_size.restype = ctypes.c_size_t
         L.mrope_attn_fwd_group.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Problem), ctypes.c_int,
@@ -281,6 +284,35 @@ def mrope_attn(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int,
     if rc != 0:
         raise _error(rc)
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mrope_attn_noalloc(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, *, text_pad: int, out,
+                       lse=None, section=(16, 24, 24), theta: float = 10000.0, eps: float = 1e-6,
+                       scale=None, kprologue="auto", rope_pairs="half"):
+    """The forward through ``mrope_attn_fwd_noalloc``: arguments as for
+    :func:`mrope_attn`, but the caller passes ``out`` (and ``lse`` [B, H, S]
+    fp32, or None) and no workspace: the library's own per-GPU scratch array
+    (``NOALLOC_SCRATCH_BYTES``) holds the intermediates. Calls that overlap
+    in time on one GPU race on that array. Returns ``out``."""
+    import torch
+
+    desc, out, _, seq_lens = _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, False,
+                                      text_pad=text_pad, section=section, theta=theta, eps=eps,
+                                      scale=scale, kprologue=kprologue, rope_pairs=rope_pairs)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (q.shape[0], q.shape[2], q.shape[1])
+                            or not lse.is_contiguous() or not lse.is_cuda):
+        raise ValueError("lse must be a contiguous float32 [B, H, S] GPU tensor")
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().mrope_attn_fwd_noalloc(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), ptr(pos),
+                                      ptr(gamma_q), ptr(gamma_k), ptr(seq_lens), out.data_ptr(), ptr(lse),
+                                      stream)
+    if rc != 0:
+        raise _error(rc)
+    return out
 
 
 def prepared_call(q, k, v, pos, gamma_q, gamma_k, seq_lens=None, **kw):

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mrope_attn.h"
 #include "attn_bf16.hpp"
@@ -303,7 +304,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 107; }
+int mrope_attn_abi_version(void) { return 108; }
 
 int mrope_attn_last_hip_error(const char** name) {
   if (name) *name = t_last_hip_error ? hipGetErrorName((hipError_t)t_last_hip_error) : "none";
@@ -322,6 +323,7 @@ const char* mrope_attn_status_string(int status) {
     case MRA_ERR_WORKSPACE: return "workspace missing or too small";
     case MRA_ERR_HIP: return "HIP launch or runtime error";
     case MRA_ERR_PARAM: return "invalid theta/eps/softmax_scale/kprologue";
+    case MRA_ERR_SCRATCH: return "problem needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -433,6 +435,57 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
     if (e == hipSuccess) e = launch_attend(&a, plan, workspace, d->head_dim, kpro, s);
   }
   return hip_status(e);
+}
+
+}  // extern "C"
+
+// ---- forward without allocation ---------------------------------------------
+// The scratch of mrope_attn_fwd_noalloc: one array per GPU, allocated with the
+// library's code object on that GPU and held until the process ends. Host
+// code never uses the name itself (on the host it is only a stand-in for the
+// symbol): it takes each device's address of the array once, below.
+static __device__ __align__(256) unsigned char scratch[MRA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// This process's current device's copy of `scratch`, looked up on the first
+// call on that device (with it current), or nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    hip_status(e != hipSuccess ? e : hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int mrope_attn_fwd_noalloc(const mra_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* pos, const float* gq, const float* gk,
+                           const int32_t* seq_lens, void* out, float* lse, void* stream) {
+  int rc = mrope_attn_validate(d, q, k, v, pos, gq, gk, seq_lens, out);
+  if (rc != MRA_OK) return rc;
+  const size_t need = mrope_attn_workspace_size(d);
+  if (need > MRA_NOALLOC_SCRATCH_BYTES) return MRA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_on_current_device())) return MRA_ERR_HIP;
+  return mrope_attn_fwd(d, q, k, v, pos, gq, gk, seq_lens, out, lse, ws, need, stream);
 }
 
 // Problems of a group call that hold at least one token, in call order;

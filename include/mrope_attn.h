@@ -49,8 +49,9 @@
  *    asynchronous; results are valid after the stream synchronises.
  *  - Errors are negative mra_status values. Every contract check runs on the
  *    host before any device work; on error nothing is launched or written.
- *  - Calls are thread-safe; the library holds no global state besides the
- *    per-thread record behind mrope_attn_last_hip_error.
+ *  - Calls are thread-safe. The library's only global state is the per-thread
+ *    record behind mrope_attn_last_hip_error and a per-device cache of the
+ *    no-allocation scratch array's address (see mrope_attn_fwd_noalloc).
  */
 #ifndef MROPE_ATTN_H
 #define MROPE_ATTN_H
@@ -72,7 +73,9 @@ typedef enum {
   MRA_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
   MRA_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
   MRA_ERR_HIP = -8,         /* a HIP launch or runtime call failed */
-  MRA_ERR_PARAM = -9        /* theta/eps/scale/kprologue/rope_pairs/gamma_per_head invalid */
+  MRA_ERR_PARAM = -9,       /* theta/eps/scale/kprologue/rope_pairs/gamma_per_head invalid */
+  MRA_ERR_SCRATCH = -10     /* mrope_attn_fwd_noalloc: the problem needs more scratch than
+                               MRA_NOALLOC_SCRATCH_BYTES */
 } mra_status;
 
 typedef enum { MRA_BF16 = 0, MRA_FP32 = 1 } mra_dtype;
@@ -140,6 +143,36 @@ int mrope_attn_fwd(const mra_desc* desc, const void* q, const void* k, const voi
                    const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
                    const int32_t* seq_lens, void* out, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Forward without any allocation ------------------------------------
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. mrope_attn_fwd_noalloc computes exactly what
+ * mrope_attn_fwd computes (the same kernels, bitwise equal results), but its
+ * scratch (the rotary table, K' and the split-tile partial results) lives in
+ * one file-scope device array of MRA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library instead of a caller workspace. Each GPU the library runs on holds
+ * its own copy of that array from the library's first use on it until the
+ * process ends. The call allocates nothing and frees nothing.
+ *
+ * It runs on the current HIP device; stream must belong to that device. The
+ * arguments, validation and errors are those of mrope_attn_fwd, plus
+ * MRA_ERR_SCRATCH (nothing launched) when mrope_attn_workspace_size(desc)
+ * exceeds MRA_NOALLOC_SCRATCH_BYTES (64 MiB: enough for one 1024px layer of
+ * 32 or 36 heads, B=1, 4608 tokens; not for the 4-item ragged batch or 12800
+ * tokens), and MRA_ERR_HIP when the array's device address cannot be
+ * obtained. Every call on one GPU uses that GPU's one array: calls that
+ * overlap in time on one GPU (on different streams, or from several host
+ * threads without ordering their streams) race and give wrong results;
+ * calls ordered on one stream are safe. The array keeps the last call's
+ * contents; no result depends on them (every byte a call reads from it was
+ * written earlier in the same call). */
+#define MRA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int mrope_attn_fwd_noalloc(const mra_desc* desc, const void* q, const void* k, const void* v,
+                           const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
+                           const int32_t* seq_lens, void* out, float* lse, void* stream);
 
 /* The two stages of mrope_attn_fwd, for callers that schedule or time them
  * separately. mrope_attn_prepare runs the prologue pass (the per-token

@@ -42,7 +42,7 @@ def test_header_declares_the_entry_points():
         "mrope_attn_abi_version", "mrope_attn_attend", "mrope_attn_bwd",
         "mrope_attn_bwd_varlen", "mrope_attn_bwd_varlen_workspace_size",
         "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
-        "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size",
+        "mrope_attn_fwd_noalloc", "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size",
         "mrope_attn_last_hip_error", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
         "mrope_attn_workspace_size", "mrope_qkv_proj", "mrope_qkv_proj_workspace_size"])
@@ -97,8 +97,8 @@ def test_struct_layouts_match_header(tmp_path, cls, struct):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 107
-    for st in range(0, -10, -1):
+    assert lib.mrope_attn_abi_version() == 108
+    for st in range(0, -11, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
     assert B.status_string(-77) == "unknown status"
@@ -241,6 +241,32 @@ def test_fwd_rejects_before_launch(lib, monkeypatch):
     assert L.mrope_attn_prepare(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, need, None) == -8
     assert L.mrope_attn_attend(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                None, FAKE, need, None) == -8
+
+
+def _noalloc(d, lse=None):
+    return B.lib().mrope_attn_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          FAKE, lse, None)
+
+
+def test_noalloc_rejects_before_any_device_call(lib):
+    # the arguments are checked like mrope_attn_fwd's; then a problem whose
+    # scratch exceeds the library's array is refused before the array is
+    # looked up (no HIP call is made on these paths)
+    assert B.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert _noalloc(desc(section=(1, 1, 1))) == -4
+    assert _noalloc(desc(head_dim=96)) == -2
+    assert _noalloc(desc(theta=0.0)) == -9
+    assert B.lib().mrope_attn_fwd_noalloc(ctypes.byref(desc()), None, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          FAKE, None, None) == -1
+    long_ = desc(batch=1, seq=12800, heads=32, text_pad=512)
+    assert B.workspace_size(long_) > B.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(long_) == -10
+    ragged = desc(batch=4, seq=4608, heads=32, text_pad=512)
+    assert _noalloc(ragged) == -10
+    # the 1024px layer (32 heads; also 36) fits
+    assert B.workspace_size(desc(batch=1, seq=4608, heads=32, text_pad=512)) <= B.NOALLOC_SCRATCH_BYTES
+    assert B.workspace_size(desc(batch=1, seq=4608, heads=36, text_pad=512)) <= B.NOALLOC_SCRATCH_BYTES
+    assert "no-allocation" in B.status_string(-10)
 
 
 def test_last_hip_error_starts_clear(lib):
