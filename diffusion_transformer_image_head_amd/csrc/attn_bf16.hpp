@@ -46,15 +46,9 @@
 namespace mra {
 
 constexpr float kRescaleLog2 = 8.0f;
-#ifndef MRA_KAHEAD
-#define MRA_KAHEAD 4
-#endif
-#ifndef MRA_PV_PACE
-#define MRA_PV_PACE 8
-#endif
-#ifndef MRA_FIXED_MAX
-#define MRA_FIXED_MAX 1
-#endif
+// operand read pacing: K' fragment reads kept in flight ahead of the Q.K'
+// MFMAs, and transposing V reads ahead of the P.V MFMAs
+constexpr int kKAhead = 4, kPvPace = 8;
 
 constexpr int kBufFlags = 0x00020000;  // raw buffer resource, 32-bit data format
 
@@ -481,12 +475,13 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
   while (t < ntiles && skipped(t)) ++t;
   refresh_neg_m();
   bool first = true;
-#if MRA_FIXED_MAX
   // QK-RMSNorm bounds every logit: |Q''.K'| <= |Q''| |K'| and |K'| <=
   // max|gamma_k| sqrt(D) (a normalised row has mean square <= 1; the margin
-  // covers K''s bf16 rounding). When that bound m stays small enough that
-  // exp2(S - m) >= exp2(-2m) is a normal float, m serves as the row's
-  // "running max" from the start: no row max, no rescaling.
+  // covers K''s bf16 rounding). When that bound m is at most 40, m serves as
+  // the row's "running max" from the start: no row max, no rescaling. Then
+  // every P = exp2(S - m) >= 2^-80, so P and the P.V products stay normal
+  // floats for any |V| >= 2^-46 (a larger m could push them into the
+  // subnormal range, which the matrix cores flush).
   bool fixed_max = false;
   if constexpr (!PRE) {
     const float* gk = a.gk + head * a.gqs;
@@ -507,7 +502,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
       // padded query rows (whose output is zero whatever they hold) neither
       // decide nor need the bound
       mf[rb] = valid_row[rb] ? sqrtf(half_swap_sum(n2)) * kb : 0.f;
-      big = big || !(mf[rb] <= 60.f);
+      big = big || !(mf[rb] <= 40.f);
     }
     if (__builtin_amdgcn_ballot_w64(big) == 0) {
       fixed_max = true;
@@ -517,9 +512,6 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
       refresh_neg_m();
     }
   }
-#else
-  constexpr bool fixed_max = false;
-#endif
 
   // S^T = K'(t) Q'^T - m from K' buffer `kpar`: all K' fragments of the tile
   // are read first so the reads overlap each other and the MFMAs using them
@@ -541,7 +533,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
           st[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[c][kb], qf[rb][c],
                                                                c == 0 ? negm_vec[rb] : st[rb][kb], 0, 0, 0);
     // keep kAhead fragment reads in flight ahead of the MFMAs
-    constexpr int kFrags = KC * NB, kAhead = MRA_KAHEAD > 0 ? MRA_KAHEAD : kFrags / 2;
+    constexpr int kFrags = KC * NB, kAhead = kKAhead;
     __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
     for (int i = 0; i < kFrags; ++i) {
@@ -641,9 +633,9 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
           for (int rb = 0; rb < RB; ++rb)
             oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[rb][kb][u], oacc[rb][db], 0, 0, 0);
         }
-    if constexpr (MRA_PV_PACE > 0) {
-      // two transposing reads per MFMA; keep MRA_PV_PACE of them in flight
-      constexpr int vM = NB * 2 * DB, vA = MRA_PV_PACE;
+    {
+      // two transposing reads per MFMA; keep kPvPace of them in flight
+      constexpr int vM = NB * 2 * DB, vA = kPvPace;
       __builtin_amdgcn_sched_group_barrier(0x100, vA, 0);
 #pragma unroll
       for (int i = 0; i < vM; ++i) {

@@ -14,11 +14,11 @@
 // dk and the gamma gradients.
 //
 // Kernels: bwd_delta_kernel (D and l2 per row); bwd_fused_kernel, one launch
-// of three independent roles: dK and dV (bwd_dkdv_body: one workgroup per 128
-// keys, 32 per wave, streaming 32-query tiles of Q'' and dO through LDS) and
-// dQ (bwd_dq_body: one workgroup per 128 queries, streaming 32-key tiles of
-// K' and V), also launchable apart as bwd_dkdv_kernel and bwd_dq_kernel;
-// bwd_dgamma_kernel (fixed-order sum of the per-workgroup gamma partials).
+// of three independent roles: dK, and dV, each recomputing S (bwd_dkdv_body:
+// one workgroup per 128 keys, 32 per wave, streaming 32-query tiles of Q''
+// and dO through LDS), and dQ (bwd_dq_body: one workgroup per 128 queries,
+// streaming 32-key tiles of K' and V); bwd_dgamma_kernel (fixed-order sum of
+// the per-workgroup gamma partials).
 // The dk/dv and dq roles work per item
 // (seq_view): a padded batch item, or one sequence of a packed layout whose
 // streams start at the sequence's first token and end with its last, so a
@@ -214,31 +214,33 @@ __device__ __forceinline__ void dgamma_partial(float (&dg)[D / 32][16], float* r
   }
 }
 
-// LDS of a dK/dV workgroup: stage p holds Q'' (q[p]), dO (o[p]) and the
+// LDS of a dK or dV workgroup: stage p holds Q'' (q[p]), dO (o[p]) and the
 // (l2, D) pairs (l[p]) of one query tile, each its own object so that a
 // stage's reads never wait on another stage's loads; vk holds the V rows of
 // the workgroup's 128 keys (row = key, chunk c at c ^ (row & 15)), read back
-// as B operands each tile instead of held in registers; red is the gamma
-// reduction's buffer.
+// as B operands each tile instead of held in registers (dK only); red is the
+// gamma reduction's buffer.
 struct DkdvLds {
-  char* q[4];
-  char* o[4];
-  float* l[4];
+  char* q[2];
+  char* o[2];
+  float* l[2];
   char* vk;
   float* red;
 };
 
-// dK and dV of workgroup `tile`: (batch, head, 128 keys), 32 keys per wave;
-// query tiles of 32 stream through LDS. INTER: interleaved rotary pairs
-// (2j, 2j + 1) in the epilogue's inverse rotation. MODE 0: both, 1: dV only,
-// 2: dK only.
+// dV (MODE 1) or dK (MODE 2) of workgroup `tile`: (batch, head, 128 keys),
+// 32 keys per wave; query tiles of 32 stream through two LDS stages (one
+// tile in flight ahead). Each role recomputes S, which keeps it within two
+// waves per SIMD. INTER: interleaved rotary pairs (2j, 2j + 1) in the
+// epilogue's inverse rotation.
 template <int D, bool INTER, int MODE>
 __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, const DkdvLds& sm) {
   constexpr int KC = D / 16, DB = D / 32, BQ = 32, TILEB = BQ * D * 2;
   constexpr int RUNS = TILEB / 1024 / 4;
-  constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
-  constexpr int NST = MODE == 0 ? 4 : 2;  // pipeline stages: NST - 1 query tiles in flight
+  constexpr bool DO_DV = MODE == 1, DO_DK = MODE == 2;
+  constexpr int NST = 2;  // pipeline stages: one query tile in flight
   constexpr int LOADS = 2 * RUNS + 1;  // direct loads per wave per tile
+  static_assert(MODE == 1 || MODE == 2, "dV or dK");
   static_assert(D == 128, "the backward kernels are written for head_dim 128");
   char* const Vk = sm.vk;
   float* const red = sm.red;
@@ -324,7 +326,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, 
     else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
-  static_assert(2 * LOADS < 16 && (NST == 2 || NST == 4), "vmcnt immediates and the step unroll below");
+  static_assert(2 * LOADS < 16, "vmcnt immediates");
 
   const int nq = (S + BQ - 1) / BQ;
   auto skipped = [&](int qt) { const int n0 = qt * BQ; return n0 >= L && min(n0 + BQ, S) <= T; };
@@ -348,17 +350,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, 
   int qt = 0;
   while (qt < nq && skipped(qt)) ++qt;
   if (all_pad) qt = nq;
-  // prologue: the first NST - 1 tiles into stages 0 .. NST - 2
+  // prologue: the first tile into stage 0
   int last = qt, ahead = 0;  // last tile issued; tiles issued after qt
-  if (qt < nq) {
-    issue(qt, Parity<0>{});
-    if constexpr (NST == 4) {
-      int t1 = next_q(qt);
-      if (t1 < nq) { issue(t1, Parity<1>{}); last = t1; ++ahead; }
-      int t2 = t1 < nq ? next_q(t1) : nq;
-      if (t2 < nq) { issue(t2, Parity<2>{}); last = t2; ++ahead; }
-    }
-  }
+  if (qt < nq) issue(qt, Parity<0>{});
 
   // tile qt sits in stage `parity`; the tile issued here goes to the stage
   // the previous tile used
@@ -441,12 +435,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, 
     step(Parity<0>{});
     if (qt >= nq) break;
     step(Parity<1>{});
-    if constexpr (NST == 4) {
-      if (qt >= nq) break;
-      step(Parity<2>{});
-      if (qt >= nq) break;
-      step(Parity<3>{});
-    }
   }
 
   // dV rows: dims db*32 + (i/4)*8 + hf*4 + i%4 of key `key`
@@ -472,31 +460,6 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs& g, const int tile, 
                            hf, dg);
   }
   dgamma_partial<D>(dg, red, g.dgk_part + (int64_t)tile * D, wave, lane);
-}
-
-// MODE 0 computes dK and dV (one wave per SIMD: dK, dV and K' take most of
-// the registers; four stages); MODE 1 only dV (S, P, dV) and MODE 2 only dK
-// (S, P, dP, dS, dK): each of those recomputes S but fits two waves per SIMD
-// (two stages).
-template <int D, bool INTER, int MODE>
-__global__ __launch_bounds__(256, MODE == 0 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs g) {
-  constexpr int TILEB = 32 * D * 2, NST = MODE == 0 ? 4 : 2;
-  __shared__ __attribute__((aligned(1024))) char Q0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char Q1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char Q2[NST == 4 ? TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) char Q3[NST == 4 ? TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) char O0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char O2[NST == 4 ? TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) char O3[NST == 4 ? TILEB : 16];
-  __shared__ __attribute__((aligned(256))) float L0[64];
-  __shared__ __attribute__((aligned(256))) float L1[64];
-  __shared__ __attribute__((aligned(256))) float L2[64];
-  __shared__ __attribute__((aligned(256))) float L3[64];
-  __shared__ __attribute__((aligned(1024))) char Vk[MODE != 1 ? 128 * D * 2 : 16];
-  __shared__ float red[4 * D];
-  const DkdvLds sm{{Q0, Q1, Q2, Q3}, {O0, O1, O2, O3}, {L0, L1, L2, L3}, Vk, red};
-  bwd_dkdv_body<D, INTER, MODE>(g, xcd_remap(blockIdx.x, gridDim.x), sm);
 }
 
 // LDS of a dQ workgroup: K' (k[p]) and V (v[p]) of key tile stage p, the
@@ -667,18 +630,6 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& g, const int tile, co
   dgamma_partial<D>(dg, red, g.dgq_part + (int64_t)tile * D, wave, lane);
 }
 
-template <int D, bool INTER>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs g) {
-  constexpr int TILEB = 32 * D * 2;
-  __shared__ __attribute__((aligned(1024))) char K0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char K1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char V0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char V1[TILEB];
-  __shared__ float red[4 * D];
-  const DqLds sm{{K0, K1}, {V0, V1}, red};
-  bwd_dq_body<D, INTER>(g, xcd_remap(blockIdx.x, gridDim.x), sm);
-}
-
 // dK, dQ and dV in one launch: the three are independent, and one grid of
 // 3 x n_wg workgroups leaves one partial round of workgroups at its end where
 // three launches of n_wg leave one each. Workgroup i runs on XCD i % 8 (the
@@ -707,7 +658,7 @@ __global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs g) {
     const DqLds sm{{B0, B1}, {B2, B3}, red};
     bwd_dq_body<D, INTER>(g, tile, sm);
   } else {
-    const DkdvLds sm{{B0, B1, nullptr, nullptr}, {B2, B3, nullptr, nullptr}, {L0, L1, nullptr, nullptr}, Vk, red};
+    const DkdvLds sm{{B0, B1}, {B2, B3}, {L0, L1}, Vk, red};
     if (role == 0) bwd_dkdv_body<D, INTER, 2>(g, tile, sm);
     else bwd_dkdv_body<D, INTER, 1>(g, tile, sm);
   }

@@ -88,37 +88,12 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
   // the matrix-core kernels work per item
   g.a.B = nseq;
   g.a.cu_seqlens = cu_seqlens;
-  // dK, dQ and dV: one launch of the three roles (MRA_BWD_FUSED), or three
-  // launches; with three, dK and dV come from one kernel that computes both
-  // (MRA_BWD_SPLIT 0) or two that each recompute S
-#ifndef MRA_BWD_FUSED
-#define MRA_BWD_FUSED 1
-#endif
-#ifndef MRA_BWD_SPLIT
-#define MRA_BWD_SPLIT 1
-#endif
+  // dK, dQ and dV: one launch of the three roles (24 x ceil(n_wg / 8)
+  // workgroups; see bwd_fused_kernel)
   const unsigned nwg = (unsigned)p.n_wg;
-  if (MRA_BWD_FUSED) {
-    const unsigned grid = 24u * ((nwg + 7u) / 8u);
-    if (g.a.inter) hipLaunchKernelGGL((mra::bwd_fused_kernel<128, true>), dim3(grid), dim3(256), 0, s, g);
-    else hipLaunchKernelGGL((mra::bwd_fused_kernel<128, false>), dim3(grid), dim3(256), 0, s, g);
-  } else if (g.a.inter) {
-    if (MRA_BWD_SPLIT) {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 1>), dim3(nwg), dim3(256), 0, s, g);
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 2>), dim3(nwg), dim3(256), 0, s, g);
-    } else {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, true, 0>), dim3(nwg), dim3(256), 0, s, g);
-    }
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, true>), dim3(nwg), dim3(256), 0, s, g);
-  } else {
-    if (MRA_BWD_SPLIT) {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 1>), dim3(nwg), dim3(256), 0, s, g);
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 2>), dim3(nwg), dim3(256), 0, s, g);
-    } else {
-      hipLaunchKernelGGL((mra::bwd_dkdv_kernel<128, false, 0>), dim3(nwg), dim3(256), 0, s, g);
-    }
-    hipLaunchKernelGGL((mra::bwd_dq_kernel<128, false>), dim3(nwg), dim3(256), 0, s, g);
-  }
+  const unsigned grid = 24u * ((nwg + 7u) / 8u);
+  if (g.a.inter) hipLaunchKernelGGL((mra::bwd_fused_kernel<128, true>), dim3(grid), dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((mra::bwd_fused_kernel<128, false>), dim3(grid), dim3(256), 0, s, g);
   if (dgamma_q || dgamma_k) {
     // per-tile partials are laid out [nseq, H, n_t, D]: a shared gamma sums
     // all of them, a per-head gamma sums head h's nseq * n_t rows

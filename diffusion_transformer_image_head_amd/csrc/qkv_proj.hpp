@@ -43,18 +43,10 @@ struct QkvArgs {
   float eps, qscale;
 };
 
-#ifndef MRA_QKV_WAVES
-#define MRA_QKV_WAVES 4
-#endif
-#ifndef MRA_QKV_KB
-#define MRA_QKV_KB 64
-#endif
-#ifndef MRA_QKV_NST
-#define MRA_QKV_NST 2
-#endif
-#ifndef MRA_QKV_TPW
-#define MRA_QKV_TPW 64
-#endif
+// The launch configuration: 4 waves of 64 tokens (two waves per head of a
+// head pair, so 128 tokens x 2 heads per workgroup), 64-wide hidden chunks,
+// 2 LDS stages.
+constexpr int kQkvWaves = 4, kQkvChunk = 64, kQkvStages = 2, kQkvTokPerWave = 64;
 
 // WAVES waves per workgroup, half of them on each head of the pair, each
 // wave TPW tokens: a workgroup computes (TPW * WAVES / 2 tokens) x (2 heads).

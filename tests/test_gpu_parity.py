@@ -9,7 +9,7 @@ all keys), which the oracle computes row by row. Invariants the method fixes
 import numpy as np
 import pytest
 
-from diffusion_transformer_image_head_amd.workloads import config_workload, make_workload
+from diffusion_transformer_image_head_amd.workloads import config_workload, make_workload, round_to_bf16
 from tests.gpu_util import (check_lse, check_parity, run_gpu, run_oracle, sample_rows, say,
                             to_dev)
 
@@ -180,11 +180,19 @@ def test_conventions_change_the_result():
 
 
 def test_prepass_and_fused_agree():
+    """The two K prologues compute K' with the same formula but sum the
+    squares of a row in different orders (per rotary pair in the prepass, per
+    8-element chunk in the fused staging), so K' can differ in the last bit
+    of a rare element. The outputs must then agree far below the parity bar:
+    rel-RMS 5e-4 and max-abs 2e-3 (under one bf16 ulp of the largest output)."""
     say("case: prepass vs fused K prologue")
     w = make_workload(**SMALL["multi_tile"], dtype="bf16", seed=330)
     a, _ = run_gpu(w, kprologue="prepass")
     b, _ = run_gpu(w, kprologue="fused")
-    assert np.max(np.abs(a - b)) < 2e-2
+    d = a - b
+    rel = float(np.sqrt((d * d).sum() / (b * b).sum()))
+    say(f"  prepass vs fused: max_abs={np.abs(d).max():.3e} rel_rms={rel:.3e}")
+    assert np.abs(d).max() <= 2e-3 and rel <= 5e-4
 
 
 # ------------------------------------------------------------------ invariants
@@ -301,6 +309,48 @@ def test_config_h4_full():
     _full_check(config_workload("h4"))
 
 
+def test_config_ragged_full():
+    """The ragged batch (4 x 4608 tokens, true text lengths 37/128/300/512
+    padded in memory to 512): every output and LSE against the oracle, and
+    exact zeros on the padded query rows."""
+    say("case: ragged config, all outputs")
+    w = config_workload("ragged")
+    out, _ = _full_check(w)
+    for b, l in enumerate(w.seq_lens):
+        assert np.all(out[b, int(l):w.text_pad] == 0)
+
+
+def test_config_long_full():
+    """The long, non-square config (512 text + 128 x 96 image = 12,800
+    tokens, sigma 1.5): every output and LSE against the oracle."""
+    say("case: long config, all outputs")
+    _full_check(config_workload("long"))
+
+
+def test_fixed_max_floor_edge():
+    """Rows whose every logit sits at the bottom of the logit bound m, with
+    m just under the fixed-max threshold: all keys are -q (positions 0, so
+    the rotation is the identity), gamma_k = 1 and gamma_q = 2.37 make every
+    log2-logit -38.7 against m = 39.0, so each P is about 2^-77.7, and V is
+    small (~1e-3). P.V products must stay normal floats; the softmax is
+    uniform, so the output is the mean of V."""
+    say("case: fixed-max floor edge (all logits at -m, small V)")
+    w = make_workload(1, 2, 128, (16, 24, 24), 256, 16, 16, dtype="bf16", seed=345)
+    q1 = w.q[:, :1]
+    w.q = np.ascontiguousarray(np.broadcast_to(q1, w.q.shape))
+    w.k = -w.q
+    w.pos = np.zeros_like(w.pos)
+    w.gamma_q = np.full_like(w.gamma_q, 2.37)
+    w.gamma_k = np.ones_like(w.gamma_k)
+    w.v = np.ascontiguousarray(round_to_bf16((w.v * 1e-3).astype(np.float32)))
+    out, lse = run_gpu(w)
+    ref, rlse = run_oracle(w)
+    check_parity(out, ref, "bf16", "fixed-max floor edge")
+    check_lse(lse, rlse)
+    mean_v = w.v.astype(np.float64).mean(axis=1, keepdims=True)
+    assert np.max(np.abs(out - mean_v)) <= 2e-5
+
+
 @pytest.mark.parametrize("shape", [
     # 4-wave workgroups: 2 x 96 heads x 3 tiles of 128 rows = 576 tiles, a
     # 64-tile last wave cut into 4 key ranges
@@ -322,7 +372,7 @@ def test_tail_split_full(shape):
     _full_check(w)
 
 
-@pytest.mark.parametrize("name", ["1024px", "ragged", "long", "h36", "2048px", "conv"])
+@pytest.mark.parametrize("name", ["h36", "2048px", "conv"])
 def test_config_sampled_rows(name):
     say(f"case: {name} config, sampled rows")
     w = config_workload(name)
