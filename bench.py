@@ -84,6 +84,22 @@ def traffic_from_profile(config: str):
         return None
 
 
+def profiles_status(config: str) -> dict:
+    """For each committed forward profile of this config: whether it was
+    taken on the current kernel sources (its kernel_source_hash), and the
+    matrix-core occupancy when the counter profile is current."""
+    cur = kernel_source_hash()
+    out = {}
+    for kind in ("kernel_trace", "hbm_traffic", "mfma_counters"):
+        rec = profile_record(f"attn_bf16_{config}_{kind}.txt")
+        if rec:
+            out[kind] = "current" if rec.get("kernel_source_hash") == cur else "stale"
+    rec = profile_record(f"attn_bf16_{config}_mfma_counters.txt")
+    if rec.get("kernel_source_hash") == cur and "mfma_busy_frac" in rec:
+        out["mfma_busy_frac"] = float(rec["mfma_busy_frac"])
+    return out
+
+
 def calibrate_copy(nbytes: int = 256 << 20, reps: int = 5):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) of the attention kernel."""
@@ -518,6 +534,7 @@ def bench_forward(args):
     rec["prewarm"] = pw
     rec["wall_s"] = round(tm["wall_s"], 4)
     rec["kernel_source_hash"] = kernel_source_hash()
+    rec["profiles"] = profiles_status(args.config)
     if not args.no_extras and args.config == "1024px":
         rec["extras"] = extras(args)
     if not args.no_cpu_baseline:

@@ -69,6 +69,13 @@ KPRO_NONE = 3
 _KPRO["none"] = KPRO_NONE
 
 
+class LaunchPlan(ctypes.Structure):
+    """Mirror of ``mra_launch_plan`` (include/mrope_attn.h)."""
+    _fields_ = [("waves", ctypes.c_int32), ("grid", ctypes.c_int32), ("xcds", ctypes.c_int32),
+                ("tiles", ctypes.c_int32), ("split_tiles", ctypes.c_int32), ("parts", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
 class MraError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"mrope_attn status {status}: {msg}")
@@ -106,6 +113,9 @@ def lib() -> ctypes.CDLL:
         L.mrope_attn_attend.restype = ctypes.c_int
         L.mrope_attn_status_string.argtypes = [ctypes.c_int]
         L.mrope_attn_status_string.restype = ctypes.c_char_p
+        L.mrope_attn_launch_plan.argtypes = [ctypes.POINTER(Desc), ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.POINTER(LaunchPlan)]
+        L.mrope_attn_launch_plan.restype = ctypes.c_int
         L.mrope_attn_last_hip_error.argtypes = [ctypes.POINTER(ctypes.c_char_p)]
         L.mrope_attn_last_hip_error.restype = ctypes.c_int
         L.mrope_attn_fwd_noalloc.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, i32p, f32p, f32p, i32p, vp,
@@ -181,6 +191,16 @@ def make_desc(batch, seq, heads, head_dim, *, text_pad, section=(16, 24, 24), th
                      ("o_stride", o_stride)):
         getattr(d, name)[:] = list(cont if st is None else st)
     return d
+
+
+def launch_plan(desc: Desc, compute_units: int = 0, xcds: int = 0) -> LaunchPlan:
+    """The bf16 attention launch for desc on a device of that shape (0: the
+    current device's); host only."""
+    p = LaunchPlan()
+    rc = lib().mrope_attn_launch_plan(ctypes.byref(desc), compute_units, xcds, ctypes.byref(p))
+    if rc != 0:
+        raise _error(rc)
+    return p
 
 
 def workspace_size(desc: Desc) -> int:

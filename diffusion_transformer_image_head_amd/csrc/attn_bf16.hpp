@@ -143,7 +143,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
   // order), then nsplit parts of each of the last n_split tiles
   int gt, part = 0, nparts = 1;
   if ((int)blockIdx.x < gp.n_whole) {
-    gt = xcd_remap(blockIdx.x, gp.n_whole);
+    gt = xcd_remap(blockIdx.x, gp.n_whole, gp.nxcd);
   } else {
     const int s_ = blockIdx.x - gp.n_whole;
     gt = gp.n_whole + s_ / gp.nsplit;

@@ -55,6 +55,7 @@ struct BwdArgs {
   float* dgq;              // [D] or null
   float* dgk;              // [D] or null
   int32_t n_t;             // 128-row tiles per (batch, head)
+  int32_t nxcd;            // XCDs of the device
 };
 
 __device__ __forceinline__ int bwd_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
@@ -632,11 +633,11 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs& g, const int tile, co
 
 // dK, dQ and dV in one launch: the three are independent, and one grid of
 // 3 x n_wg workgroups leaves one partial round of workgroups at its end where
-// three launches of n_wg leave one each. Workgroup i runs on XCD i % 8 (the
-// dispatcher's round robin); XCD x takes, in order, its contiguous share of
-// the dK tiles, then of the dQ tiles, then of the dV tiles (the lightest role
-// last), each share ceil(n_wg / 8) tiles (the grid is 24 x that; workgroups
-// past the last tile exit). The roles share one set of LDS objects, so the
+// three launches of n_wg leave one each. Workgroup i runs on XCD i % nxcd
+// (the dispatcher's round robin); XCD x takes, in order, its contiguous share
+// of the dK tiles, then of the dQ tiles, then of the dV tiles (the lightest
+// role last), each share ceil(n_wg / nxcd) tiles (the grid is 3 x nxcd x
+// that; workgroups past the last tile exit). The roles share one set of LDS objects, so the
 // kernel needs the largest role's LDS, not their sum.
 template <int D, bool INTER>
 __global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs g) {
@@ -649,9 +650,9 @@ __global__ __launch_bounds__(256, 2) void bwd_fused_kernel(BwdArgs g) {
   __shared__ __attribute__((aligned(256))) float L1[64];
   __shared__ __attribute__((aligned(1024))) char Vk[128 * D * 2];
   __shared__ float red[4 * D];
-  const int n_wg = g.a.B * g.a.H * g.n_t;
-  const int per = (n_wg + 7) / 8;
-  const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int n_wg = g.a.B * g.a.H * g.n_t, nx = g.nxcd;
+  const int per = (n_wg + nx - 1) / nx;
+  const int x = blockIdx.x % nx, j = blockIdx.x / nx;
   const int role = j / per, tile = x * per + j % per;
   if (tile >= n_wg) return;
   if (role == 1) {

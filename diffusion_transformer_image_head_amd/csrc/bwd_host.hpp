@@ -73,6 +73,7 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
   g.dgk_part = (float*)(w + p.off_gk);
   g.dgq = dgamma_q; g.dgk = dgamma_k;
   g.n_t = p.n_t;
+  g.nxcd = current_device_shape().xcds;
 
   // the row-wise passes run over the whole layout (every token of a packed
   // slice): K' and the rotary table, then Q'' = c2 * rope(rmsnorm(q)) (same
@@ -88,10 +89,10 @@ static int bwd_run(const mra_desc* d, int nseq, int maxlen, const int32_t* seq_l
   // the matrix-core kernels work per item
   g.a.B = nseq;
   g.a.cu_seqlens = cu_seqlens;
-  // dK, dQ and dV: one launch of the three roles (24 x ceil(n_wg / 8)
-  // workgroups; see bwd_fused_kernel)
-  const unsigned nwg = (unsigned)p.n_wg;
-  const unsigned grid = 24u * ((nwg + 7u) / 8u);
+  // dK, dQ and dV: one launch of the three roles (3 x nxcd x
+  // ceil(n_wg / nxcd) workgroups; see bwd_fused_kernel)
+  const unsigned nwg = (unsigned)p.n_wg, nx = (unsigned)g.nxcd;
+  const unsigned grid = 3u * nx * ((nwg + nx - 1u) / nx);
   if (g.a.inter) hipLaunchKernelGGL((mra::bwd_fused_kernel<128, true>), dim3(grid), dim3(256), 0, s, g);
   else hipLaunchKernelGGL((mra::bwd_fused_kernel<128, false>), dim3(grid), dim3(256), 0, s, g);
   if (dgamma_q || dgamma_k) {

@@ -86,6 +86,7 @@ struct Group {
   int32_t n_whole;
   int32_t n_split;
   int32_t nsplit;
+  int32_t nxcd;   // XCDs of the device (workgroups are dealt to them in turn)
   float* part;
 };
 
@@ -125,13 +126,13 @@ __device__ __forceinline__ int axis_pos(const Rope& r, int j, int pt, int ph, in
   return j < r.sec_t ? pt : (j < r.sec_th ? ph : pw);
 }
 
-// Bijective remap of a linear workgroup id so consecutive logical tiles land on
-// the same XCD: the hardware deals workgroups round-robin over 8 XCDs, so ids
-// i, i+8, i+16, ... share an XCD; give each XCD a contiguous logical range.
-__device__ __forceinline__ int xcd_remap(int i, int n) {
-  constexpr int kXcd = 8;
-  const int q = n / kXcd, r = n % kXcd;
-  const int x = i % kXcd, local = i / kXcd;
+// Bijective remap of a linear workgroup id i < n so consecutive logical tiles
+// land on the same XCD: the hardware deals workgroups round-robin over the
+// device's nx XCDs, so ids i, i+nx, i+2nx, ... share an XCD; give each XCD a
+// contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int i, int n, int nx) {
+  const int q = n / nx, r = n % nx;
+  const int x = i % nx, local = i / nx;
   return x * q + (x < r ? x : r) + local;
 }
 

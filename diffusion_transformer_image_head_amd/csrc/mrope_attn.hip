@@ -18,32 +18,48 @@ namespace {
 
 using mra::Args;
 
-// Waves per attention workgroup: 0 chooses per problem (make_plan); 4 or 8
-// forces one.
-#ifndef MRA_WAVES
-#define MRA_WAVES 0
-#endif
-#ifndef MRA_BLOCK_N
-#define MRA_BLOCK_N 64
-#endif
-constexpr int kBlockN = MRA_BLOCK_N;  // keys per K/V tile
-#ifndef MRA_ROW_BLOCKS
-#define MRA_ROW_BLOCKS 1
-#endif
-constexpr int kRowBlocks = MRA_ROW_BLOCKS;  // 32-row blocks per wave
+constexpr int kBlockN = 64;     // keys per K/V tile
+constexpr int kRowBlocks = 1;   // 32-row blocks per wave
 constexpr int kFp32BlockM = 64;
 constexpr size_t kWsAlign = 256;
-// Attention workgroups of w waves resident at once on an MI355X (256 CUs;
-// two per CU below 8 waves, one from 8).
-constexpr int kComputeUnits = 256;
-constexpr int resident_slots(int w) { return kComputeUnits * (w * kRowBlocks >= 8 ? 1 : 2); }
-// Workgroups the split tiles of the last wave are spread over: one per CU
-// (measured faster than filling both slots of every CU, which doubles the
-// partial results the merge pass reads).
-#ifndef MRA_SPLIT_TARGET
-#define MRA_SPLIT_TARGET kComputeUnits
-#endif
-constexpr int kSplitTarget = MRA_SPLIT_TARGET;
+// A split part keeps at least this many key tiles (shorter parts lose more to
+// their own prologue and the merge than the idle slots they fill).
+constexpr int kMinPartKeyTiles = 24;
+constexpr int kMaxXcds = 16;
+
+// Compute units and XCDs of a device, for the attention launch plan.
+struct DeviceShape {
+  int cus, xcds;
+};
+constexpr DeviceShape kDefaultShape{256, 8};  // MI355X
+constexpr int kMaxDevices = 64;
+
+// The current device's shape, queried once per device and cached; the
+// MI355X's when no device can be queried (host-only use, e.g. sizing a
+// workspace on a machine without a GPU).
+DeviceShape current_device_shape() {
+  static std::mutex mu;
+  static DeviceShape cache[kMaxDevices];
+  static bool have[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultShape;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    DeviceShape d = kDefaultShape;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) d.cus = v;
+    v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && v > 0) d.xcds = v;
+    else d.xcds = 1;
+    (void)hipGetLastError();
+    cache[dev] = d;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
 
 // hipError_t behind the calling thread's most recent MRA_ERR_HIP
 // (mrope_attn_last_hip_error), 0 if none yet.
@@ -107,9 +123,10 @@ int check_strides(const int64_t* st, int dtype) {
 // workgroups and merged by a second kernel. The workspace holds, problem after
 // problem, the (cos, sin) table [B, S, D/2] float2 and (prepass K prologue
 // only) K' [B, H, S, D] bf16, then the fp32 split-tile records; every piece
-// starts 256-byte aligned.
+// starts 256-byte aligned. The resident slots and the XCD count come from the
+// device's shape.
 struct Plan {
-  int n, waves;
+  int n, waves, grid, tiles, nxcd;
   int n_qt[MRA_MAX_GROUP];
   int tile_end[MRA_MAX_GROUP];
   int n_whole, n_split, nsplit;
@@ -129,11 +146,16 @@ size_t kprime_bytes(const mra_desc* d) {
 // Problem i's query tiles cover qbatch[i] items of qlen[i] rows (defaults:
 // the descriptor's batch and seq; a packed layout passes its item count and
 // longest item), its table and K' the descriptor's [batch, seq] layout.
-Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
+Plan make_plan(const mra_desc* const* ds, int n, DeviceShape dev, const int* qbatch = nullptr,
                const int* qlen = nullptr) {
   Plan p;
   std::memset(&p, 0, sizeof(p));
   p.n = n;
+  const int cus = std::max(dev.cus, 1);
+  p.nxcd = std::min(std::max(dev.xcds, 1), kMaxXcds);
+  // attention workgroups of w waves resident at once: two per CU below 8
+  // waves, one from 8
+  auto resident_slots = [&](int w) { return cus * (w * kRowBlocks >= 8 ? 1 : 2); };
   // 8-wave workgroups (256 query rows, one per CU) when the problems hold at
   // least 2.5 rounds of them, or one partial round that the third split rule
   // below cuts into 3 key ranges; 4-wave ones (128 rows, two per CU)
@@ -149,8 +171,8 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
     kt_min = std::min(kt_min, (ql + kBlockN - 1) / kBlockN);
   }
   const int64_t s8 = resident_slots(8);
-  const bool cut_round8 = 4 * tiles8 > s8 && 5 * tiles8 <= 3 * s8 && kt_min >= 3 * 24;
-  const int waves = MRA_WAVES ? MRA_WAVES : ((2 * tiles8 >= 5 * s8 || cut_round8) ? 8 : 4);
+  const bool cut_round8 = 4 * tiles8 > s8 && 5 * tiles8 <= 3 * s8 && kt_min >= 3 * kMinPartKeyTiles;
+  const int waves = (2 * tiles8 >= 5 * s8 || cut_round8) ? 8 : 4;
   const int bm = waves * 32 * kRowBlocks, slots = resident_slots(waves);
   p.waves = waves;
   int tiles = 0, ktiles = 1 << 30;
@@ -170,31 +192,36 @@ Plan make_plan(const mra_desc* const* ds, int n, const int* qbatch = nullptr,
   int r = tiles >= slots ? tiles % slots : tiles;
   int k = 1;
   // split when the last wave would leave at least half of the compute units
-  // idle (a unit running one workgroup instead of two is not idle), or, after
-  // whole waves, when it holds a few more tiles than there are units (a few
-  // units would run two tiles while the rest run one: halves even them out;
-  // measured on last waves of 192 to 416 tiles, it pays only in that band)
-  if (r > 0 && 4 * r <= slots) k = std::min(std::min(kSplitTarget / r, mra::kMaxSplit), ktiles);
-  else if (tiles >= slots && r > kComputeUnits && 4 * r <= 5 * kComputeUnits) k = std::min(2, ktiles);
+  // idle (a unit running one workgroup instead of two is not idle), spreading
+  // the parts over one workgroup per CU (measured faster than filling both
+  // slots of every CU, which doubles the partial results the merge reads), or,
+  // after whole waves, when it holds a few more tiles than there are units (a
+  // few units would run two tiles while the rest run one: halves even them
+  // out; measured on last waves of 192 to 416 tiles, it pays only in that
+  // band)
+  if (r > 0 && 4 * r <= slots) k = std::min(std::min(cus / r, mra::kMaxSplit), ktiles);
+  else if (tiles >= slots && r > cus && 4 * r <= 5 * cus) k = std::min(2, ktiles);
   // a single wave too full for the first rule but at most 3/5 of the slots
   // (say one GPU's 4 or 8 heads of a head-sharded layer): every tile in 3 key
   // ranges, when each range keeps at least 24 key tiles (measured at 4608
   // tokens: 144 tiles 90.6 -> 66.3 us, 288 tiles 129.6 -> 119.0 us; 2 or 4
   // ranges less; 512px, 20 key tiles, loses with any cut)
-  else if (tiles < slots && 5 * r <= 3 * slots && ktiles >= 3 * 24) k = std::min(3, mra::kMaxSplit);
+  else if (tiles < slots && 5 * r <= 3 * slots && ktiles >= 3 * kMinPartKeyTiles) k = std::min(3, mra::kMaxSplit);
   if (k < 2) { r = 0; k = 1; }
   p.n_split = r;
   p.nsplit = k;
   p.n_whole = tiles - r;
+  p.tiles = tiles;
+  p.grid = p.n_whole + p.n_split * p.nsplit;
   p.off_part = off;
   const size_t rec_floats = (size_t)kRowBlocks * waves * 64 * (ds[0]->head_dim / 2 + 2);
   p.bytes = off + round_up((size_t)r * k * rec_floats * sizeof(float), kWsAlign);
   return p;
 }
 
-size_t workspace_bytes(const mra_desc* d) {
+size_t workspace_bytes(const mra_desc* d, DeviceShape dev) {
   if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0) return 0;
-  return make_plan(&d, 1).bytes;
+  return make_plan(&d, 1, dev).bytes;
 }
 
 void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const void* v,
@@ -243,8 +270,7 @@ hipError_t launch_prologue_bf16(Args& a, int kpro, hipStream_t s) {
 }
 
 template <int D, int W, int G>
-hipError_t launch_attend_waves(const mra::Group<G>& g, int kpro, hipStream_t s) {
-  const unsigned grid = (unsigned)(g.n_whole + g.n_split * g.nsplit);
+hipError_t launch_attend_waves(const mra::Group<G>& g, int grid, int kpro, hipStream_t s) {
   if (kpro == MRA_KPRO_PREPASS)
     hipLaunchKernelGGL((mra::attn_bf16_kernel<D, W, kBlockN, kRowBlocks, 0, G>), dim3(grid), dim3(W * 64), 0, s, g);
   else if (kpro == MRA_KPRO_FUSED)
@@ -258,8 +284,8 @@ hipError_t launch_attend_waves(const mra::Group<G>& g, int kpro, hipStream_t s) 
   return hipGetLastError();
 }
 template <int D, int G>
-hipError_t launch_attend_group(const mra::Group<G>& g, int kpro, int waves, hipStream_t s) {
-  return waves == 8 ? launch_attend_waves<D, 8>(g, kpro, s) : launch_attend_waves<D, 4>(g, kpro, s);
+hipError_t launch_attend_group(const mra::Group<G>& g, int grid, int kpro, int waves, hipStream_t s) {
+  return waves == 8 ? launch_attend_waves<D, 8>(g, grid, kpro, s) : launch_attend_waves<D, 4>(g, grid, kpro, s);
 }
 static_assert(sizeof(mra::Group<MRA_MAX_GROUP>) <= 4096, "kernel argument size");
 
@@ -276,6 +302,7 @@ void make_group(mra::Group<G>& g, const Args* as, const Plan& p, void* workspace
   g.n_whole = p.n_whole;
   g.n_split = p.n_split;
   g.nsplit = p.nsplit;
+  g.nxcd = p.nxcd;
   g.part = p.n_split ? (float*)((char*)workspace + p.off_part) : nullptr;
 }
 
@@ -283,11 +310,13 @@ hipError_t launch_attend(const Args* as, const Plan& p, void* workspace, int D, 
   if (p.n == 1) {
     mra::Group<1> g;
     make_group(g, as, p, workspace);
-    return D == 128 ? launch_attend_group<128>(g, kpro, p.waves, s) : launch_attend_group<64>(g, kpro, p.waves, s);
+    return D == 128 ? launch_attend_group<128>(g, p.grid, kpro, p.waves, s)
+                    : launch_attend_group<64>(g, p.grid, kpro, p.waves, s);
   }
   mra::Group<MRA_MAX_GROUP> g;
   make_group(g, as, p, workspace);
-  return D == 128 ? launch_attend_group<128>(g, kpro, p.waves, s) : launch_attend_group<64>(g, kpro, p.waves, s);
+  return D == 128 ? launch_attend_group<128>(g, p.grid, kpro, p.waves, s)
+                  : launch_attend_group<64>(g, p.grid, kpro, p.waves, s);
 }
 
 // qlen: rows per item (a.S for the padded layout, the longest item for a
@@ -357,9 +386,28 @@ int mrope_attn_validate(const mra_desc* d, const void* q, const void* k, const v
   return MRA_OK;
 }
 
+int mrope_attn_launch_plan(const mra_desc* d, int32_t cus, int32_t xcds, mra_launch_plan* out) {
+  if (!out) return MRA_ERR_NULL;
+  std::memset(out, 0, sizeof(*out));
+  const int rc = check_desc(d);
+  if (rc != MRA_OK) return rc;
+  if (d->dtype != MRA_BF16) return MRA_ERR_UNSUPPORTED;
+  if (d->batch == 0 || d->seq == 0) return MRA_OK;
+  const DeviceShape dev = cus > 0 ? DeviceShape{cus, xcds > 0 ? xcds : 1} : current_device_shape();
+  const Plan p = make_plan(&d, 1, dev);
+  out->waves = p.waves;
+  out->grid = p.grid;
+  out->xcds = p.nxcd;
+  out->tiles = p.tiles;
+  out->split_tiles = p.n_split;
+  out->parts = p.nsplit;
+  out->workspace_bytes = p.bytes;
+  return MRA_OK;
+}
+
 size_t mrope_attn_workspace_size(const mra_desc* d) {
   if (check_desc(d) != MRA_OK) return 0;
-  return workspace_bytes(d);
+  return workspace_bytes(d, current_device_shape());
 }
 
 // Shared front half of the three launching entry points: validation,
@@ -373,14 +421,15 @@ static int prepare_call(const mra_desc* d, const void* q, const void* k, const v
   empty = d->batch == 0 || d->seq == 0;
   if (empty) return MRA_OK;
   if (lse && !aligned(lse, 4)) return MRA_ERR_STRIDE;
-  const size_t need = workspace_bytes(d);
+  const DeviceShape dev = current_device_shape();
+  const size_t need = workspace_bytes(d, dev);
   if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MRA_ERR_WORKSPACE;
   const char* fi = std::getenv("MRA_FAULT_INJECT");
   if (fi && std::strcmp(fi, "launch") == 0) return MRA_ERR_HIP;
   clear_stale_hip_error();
   fill_args(a, d, q, k, v, pos, gq, gk, seq_lens, out, lse);
   if (d->dtype == MRA_BF16) {
-    plan = make_plan(&d, 1);
+    plan = make_plan(&d, 1, dev);
     bind_workspace(a, d, plan, 0, workspace);
   }
   return MRA_OK;
@@ -447,7 +496,6 @@ int mrope_attn_fwd(const mra_desc* d, const void* q, const void* k, const void* 
 static __device__ __align__(256) unsigned char scratch[MRA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
 
@@ -517,7 +565,7 @@ size_t mrope_attn_group_workspace_size(const mra_desc* descs, int n) {
     if (descs[i].batch > 0 && descs[i].seq > 0) ds[m++] = &descs[i];
   }
   if (m == 0 || descs[0].dtype != MRA_BF16) return 0;
-  return make_plan(ds, m).bytes;
+  return make_plan(ds, m, current_device_shape()).bytes;
 }
 
 int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n, void* workspace,
@@ -546,7 +594,7 @@ int mrope_attn_fwd_group(const mra_desc* descs, const mra_problem* probs, int n,
       e = D == 128 ? launch_fp32<128>(as[j], s, as[j].S) : launch_fp32<64>(as[j], s, as[j].S);
     return hip_status(e);
   }
-  const Plan plan = make_plan(ds, m);
+  const Plan plan = make_plan(ds, m, current_device_shape());
   const int kpro = resolve_kprologue(ds[0]);
   for (int j = 0; j < m && e == hipSuccess; ++j) {
     bind_workspace(as[j], ds[j], plan, j, workspace);
@@ -576,7 +624,7 @@ size_t mrope_attn_varlen_workspace_size(const mra_desc* d, int32_t max_seqlen) {
   if (d->dtype != MRA_BF16 || d->batch == 0 || d->seq == 0 || max_seqlen == 0) return 0;
   const mra_desc* ds[1] = {&lay};
   const int qb = d->batch, ql = max_seqlen;
-  return make_plan(ds, 1, &qb, &ql).bytes;
+  return make_plan(ds, 1, current_device_shape(), &qb, &ql).bytes;
 }
 
 int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const void* v,
@@ -607,7 +655,7 @@ int mrope_attn_fwd_varlen(const mra_desc* d, const void* q, const void* k, const
   } else {
     const mra_desc* ds[1] = {&lay};
     const int qb = d->batch, ql = max_seqlen;
-    const Plan plan = make_plan(ds, 1, &qb, &ql);
+    const Plan plan = make_plan(ds, 1, current_device_shape(), &qb, &ql);
     bind_workspace(a, &lay, plan, 0, workspace);
     const int kpro = resolve_kprologue(d);
     // the prologue pass runs over the packed layout (one item of seq tokens)

@@ -81,6 +81,7 @@ int mrope_qkv_proj(const mra_qkv_desc* d, const void* x, const uint8_t* w8, cons
   g.out[0] = (uint16_t*)q_out; g.out[1] = (uint16_t*)k_out; g.out[2] = (uint16_t*)v_out;
   const int64_t* st[3] = {d->q_stride, d->k_stride, d->v_stride};
   for (int i = 0; i < 3; ++i) { g.os[i][0] = st[i][0]; g.os[i][1] = st[i][1]; }
+  g.nxcd = current_device_shape().xcds;
   g.M = d->tokens;
   g.hidden = d->hidden;
   g.H = d->heads;

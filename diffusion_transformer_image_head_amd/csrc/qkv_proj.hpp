@@ -38,6 +38,7 @@ struct QkvArgs {
   uint16_t* out[3];       // q_op, k_op, v: [M, H, D] with (token, head) strides
   int64_t os[3][2];
   int32_t M, hidden, H, n_mt;
+  int32_t nxcd;           // XCDs of the device
   int32_t gqs;            // elements between two heads' gamma rows (0: shared [D])
   int32_t inter;          // rotary pairs (2j, 2j + 1) instead of (j, j + D/2)
   float eps, qscale;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(WAVES * 64, (WAVES == 4 && TPW <= 64) ? 2 : 1) void
   // few times instead of x once per head pair.
   constexpr int GT = 8;
   const int nhp = (3 * g.H + 1) / 2;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x, g.nxcd);
   const int full = g.n_mt / GT;
   int mt, hp;
   if (tile < full * GT * nhp) {

@@ -174,6 +174,33 @@ int mrope_attn_fwd_noalloc(const mra_desc* desc, const void* q, const void* k, c
                            const int32_t* pos_thw, const float* gamma_q, const float* gamma_k,
                            const int32_t* seq_lens, void* out, float* lse, void* stream);
 
+/* ---- The launch plan (host only) -----------------------------------------
+ *
+ * The bf16 attention launches one workgroup per query tile, dealt so that the
+ * tiles each XCD runs are neighbours (shared K'/V in its L2); when the last
+ * round of workgroups would leave most of the device idle, its tiles are cut
+ * into key-range parts merged by a second kernel. The plan depends on the
+ * device's compute units and XCDs, which the library queries once per
+ * device; mrope_attn_workspace_size and every launching call use the current
+ * device's. mrope_attn_launch_plan reports the plan for a given device shape
+ * without touching a device: compute_units <= 0 asks for the current
+ * device's (the MI355X's 256 CUs in 8 XCDs when no device can be queried);
+ * xcds <= 0 means 1. Returns the descriptor checks' error, MRA_ERR_NULL for
+ * a NULL plan, MRA_ERR_UNSUPPORTED for fp32 (which has no such plan), else
+ * MRA_OK; an empty problem gives a zero plan. */
+typedef struct {
+  int32_t waves;            /* waves per attention workgroup: 4 (128 query rows) or 8 (256) */
+  int32_t grid;             /* attention workgroups launched */
+  int32_t xcds;             /* XCDs the workgroups are dealt to */
+  int32_t tiles;            /* query tiles */
+  int32_t split_tiles;      /* tiles computed as key-range parts and merged */
+  int32_t parts;            /* key-range parts per split tile (1: no split) */
+  uint64_t workspace_bytes; /* mrope_attn_workspace_size on such a device */
+} mra_launch_plan;
+
+int mrope_attn_launch_plan(const mra_desc* desc, int32_t compute_units, int32_t xcds,
+                           mra_launch_plan* plan);
+
 /* The two stages of mrope_attn_fwd, for callers that schedule or time them
  * separately. mrope_attn_prepare runs the prologue pass (the per-token
  * rotary (cos, sin) table, plus K' for MRA_KPRO_PREPASS) into the workspace;

