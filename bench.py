@@ -47,12 +47,21 @@ DATA = "synthetic (seeded N(0,1) q/k/v, U[0.5,1.5) gammas; no dataset or weights
 
 
 # sources the forward attention's kernels and launches are built from
-FORWARD_SOURCES = ("attn_bf16.hpp", "mra_common.hpp", "mrope_attn.hip", "prologue.hpp")
+# Kernel sources each profiled path is built from (host files included: they
+# choose the launch configuration).
+SOURCES = {
+    "forward": ("attn_bf16.hpp", "mra_common.hpp", "mrope_attn.hip", "prologue.hpp"),
+    "backward": ("attn_bwd.hpp", "bwd_host.hpp", "attn_bf16.hpp", "mra_common.hpp", "mrope_attn.hip",
+                 "prologue.hpp"),
+    "qkv": ("qkv_proj.hpp", "qkv_host.hpp", "attn_bf16.hpp", "mra_common.hpp", "mrope_attn.hip",
+            "prologue.hpp"),
+}
+FORWARD_SOURCES = SOURCES["forward"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str = "forward") -> str:
     h = hashlib.sha256()
-    for name in FORWARD_SOURCES:
+    for name in SOURCES[path]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -98,6 +107,15 @@ def profiles_status(config: str) -> dict:
     if rec.get("kernel_source_hash") == cur and "mfma_busy_frac" in rec:
         out["mfma_busy_frac"] = float(rec["mfma_busy_frac"])
     return out
+
+
+def path_profile_status(name: str, path: str) -> str:
+    """'current' when the committed summary `name` was taken on the current
+    sources of `path` (backward or qkv), 'stale' otherwise, 'absent'."""
+    rec = profile_record(name)
+    if not rec:
+        return "absent"
+    return "current" if rec.get("kernel_source_hash") == kernel_source_hash(path) else "stale"
 
 
 def calibrate_copy(nbytes: int = 256 << 20, reps: int = 5):
@@ -397,6 +415,9 @@ def bench_qkv(args):
     rec["call_ms"] = summarize(tp["total"])
     am = float(np.median(ta["total"]))
     rec["attention_on_operands"] = {"ms_median": round(am, 5), "TFLOP/s": round(tflops(att_flops, am), 3)}
+    rec["kernel_source_hash"] = kernel_source_hash("qkv")
+    if args.config == "1024px":
+        rec["profile"] = path_profile_status("qkv_proj_1024px_kernel_trace.txt", "qkv")
     print(json.dumps(rec), flush=True)
 
 
@@ -416,6 +437,9 @@ def bench_bwd(args):
                                kernel_ms=round(med, 5))
     rec["prewarm"] = pw
     rec["call_ms"] = summarize(tb["total"])
+    rec["kernel_source_hash"] = kernel_source_hash("backward")
+    if args.config == "1024px":
+        rec["profile"] = path_profile_status("attn_bwd_1024px_kernel_trace.txt", "backward")
     print(json.dumps(rec), flush=True)
 
 
@@ -489,14 +513,18 @@ def extras(args) -> dict:
     b = timed_calls([step], warm, steps)
     bm = float(np.median(b["total"]))
     res["backward_1024px"] = {"ms_median": round(bm, 5), "TFLOP/s": round(tflops(flops, bm), 3),
-                              "what": "dq, dk, dv, dgammas; FLOPs 2.5x the forward's"}
+                              "what": "dq, dk, dv, dgammas; FLOPs 2.5x the forward's",
+                              "kernel_source_hash": kernel_source_hash("backward"),
+                              "profile": path_profile_status("attn_bwd_1024px_kernel_trace.txt", "backward")}
     torch.cuda.empty_cache()
     _, flops, proj, _, _ = setup_qkv("1024px")
     p = timed_calls([proj], warm, steps)
     pm = float(np.median(p["total"]))
     res["qkv_proj_1024px"] = {"ms_median": round(pm, 5), "TFLOP/s": round(tflops(flops, pm), 3),
                               "what": "x [4608, 4096] bf16 x fp8 e4m3 W [12288, 4096] with row scales, "
-                                      "norm/rotation epilogue"}
+                                      "norm/rotation epilogue",
+                              "kernel_source_hash": kernel_source_hash("qkv"),
+                              "profile": path_profile_status("qkv_proj_1024px_kernel_trace.txt", "qkv")}
     for r in res.values():
         r["frac"] = round(r["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
     res["protocol"] = f"{warm} warm-up + {steps} timed calls each, after the headline region"
