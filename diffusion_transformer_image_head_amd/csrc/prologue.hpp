@@ -16,7 +16,8 @@ namespace mra {
 // K' = bf16(pscale * rope(rmsnorm(K))) into [B, H, S, D], plus (when a.cs is
 // set) the (cos, sin) table [B, S, D/2]. One wave per token; 16 lanes
 // per head row, so a wave covers 4 heads per step. The token's rotary angles
-// are shared by all heads and computed once per lane with the accurate sincosf.
+// are shared by all heads: each is computed once, by one lane, with the
+// accurate sincosf.
 // Lane `sub` owns rotary pairs sub*PPL .. +PPL-1: with half-split pairs their
 // elements are the runs [sub*PPL, +PPL) and [D/2 + sub*PPL, +PPL); with
 // interleaved pairs, the one run [2*sub*PPL, +2*PPL). K' keeps the element
@@ -37,19 +38,34 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
   const int o1 = inter ? 2 * sub * PPL : sub * PPL;
   const int o2 = inter ? o1 + 1 : o1 + HALF;
 
-  float cs[PPL], sn[PPL];
-#pragma unroll
-  for (int p = 0; p < PPL; ++p) {
-    const int j = sub * PPL + p;
-    const float ang = (float)axis_pos(a.rope, j, pt, ph, pw) * a.rope.inv_freq[j];
-    sincosf(ang, &sn[p], &cs[p]);
-    // the same rotation feeds the Q side inside the attention kernel
-    if (hq == 0 && a.cs) a.cs[(int64_t)tok * HALF + j] = make_float2(cs[p], sn[p]);
-  }
   const uint16_t* kb = (const uint16_t*)a.k + b * a.ks0 + s * a.ks1;
-  for (int h = hq; h < a.H; h += 4) {
+  // Raw K words of head h for this lane's pairs (first members then second
+  // members for half-split pairs; the pairs in order for interleaved ones),
+  // and the gammas of those elements. Head group h + 4's loads are issued
+  // before head group h is computed, the first before the angles, so two
+  // groups' loads are in flight per wave.
+  auto load_k = [&](int h) {
+    const uint16_t* src = kb + h * a.ks2;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if constexpr (PPL == 4) {
+      if (inter) {
+        w = *(const u32x4*)(src + o1);
+      } else {
+        const u32x2 w1 = *(const u32x2*)(src + o1), w2 = *(const u32x2*)(src + o2);
+        w = u32x4{w1[0], w1[1], w2[0], w2[1]};
+      }
+    } else {
+      if (inter) {
+        const u32x2 v = *(const u32x2*)(src + o1);
+        w = u32x4{v[0], v[1], 0u, 0u};
+      } else {
+        w = u32x4{*(const uint32_t*)(src + o1), *(const uint32_t*)(src + o2), 0u, 0u};
+      }
+    }
+    return w;
+  };
+  auto load_g = [&](int h, float (&g1)[PPL], float (&g2)[PPL]) {
     const float* gk = a.gk + h * a.gqs;
-    float g1[PPL], g2[PPL];
     if (inter) {
       float gv[2 * PPL];
 #pragma unroll
@@ -60,30 +76,48 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
 #pragma unroll
       for (int p = 0; p < PPL; ++p) { g1[p] = gk[o1 + p]; g2[p] = gk[o2 + p]; }
     }
-    const uint16_t* src = kb + h * a.ks2;
+  };
+  u32x4 wc = {0u, 0u, 0u, 0u};
+  float g1[PPL], g2[PPL];
+  if (hq < a.H) {
+    wc = load_k(hq);
+    load_g(hq, g1, g2);
+  }
+
+  // One rotary pair per lane (lane mod HALF), then each lane gathers the
+  // (cos, sin) of its own pairs from the lanes that computed them.
+  float cs[PPL], sn[PPL];
+  {
+    const int j = lane % HALF;
+    const float ang = (float)axis_pos(a.rope, j, pt, ph, pw) * a.rope.inv_freq[j];
+    float s1, c1;
+    sincosf(ang, &s1, &c1);
+    // the same rotation feeds the Q side inside the attention kernel
+    if (lane < HALF && a.cs) a.cs[(int64_t)tok * HALF + j] = make_float2(c1, s1);
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) {
+      cs[p] = __shfl(c1, sub * PPL + p, 64);
+      sn[p] = __shfl(s1, sub * PPL + p, 64);
+    }
+  }
+  for (int h = hq; h < a.H; h += 4) {
+    u32x4 wn = {0u, 0u, 0u, 0u};
+    float n1[PPL] = {}, n2[PPL] = {};
+    if (h + 4 < a.H) {
+      wn = load_k(h + 4);
+      load_g(h + 4, n1, n2);
+    }
     float x1[PPL], x2[PPL];
     if (inter) {
-      // PPL pairs = 2 * PPL consecutive elements, first members at even slots
-      uint32_t w[PPL];
-      if constexpr (PPL == 4) {
-        const u32x4 v = *(const u32x4*)(src + o1);
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-      } else {
-        const u32x2 v = *(const u32x2*)(src + o1);
-        w[0] = v[0]; w[1] = v[1];
-      }
 #pragma unroll
-      for (int p = 0; p < PPL; ++p) { x1[p] = bf16_lo(w[p]); x2[p] = bf16_hi(w[p]); }
-    } else if constexpr (PPL == 4) {
-      const u32x2 w1 = *(const u32x2*)(src + o1);
-      const u32x2 w2 = *(const u32x2*)(src + o2);
-      x1[0] = bf16_lo(w1[0]); x1[1] = bf16_hi(w1[0]); x1[2] = bf16_lo(w1[1]); x1[3] = bf16_hi(w1[1]);
-      x2[0] = bf16_lo(w2[0]); x2[1] = bf16_hi(w2[0]); x2[2] = bf16_lo(w2[1]); x2[3] = bf16_hi(w2[1]);
+      for (int p = 0; p < PPL; ++p) { x1[p] = bf16_lo(wc[p]); x2[p] = bf16_hi(wc[p]); }
     } else {
-      const uint32_t w1 = *(const uint32_t*)(src + o1);
-      const uint32_t w2 = *(const uint32_t*)(src + o2);
-      x1[0] = bf16_lo(w1); x1[1] = bf16_hi(w1);
-      x2[0] = bf16_lo(w2); x2[1] = bf16_hi(w2);
+#pragma unroll
+      for (int p = 0; p < PPL; ++p) {
+        const uint32_t u1 = wc[p / 2], u2 = wc[PPL / 2 + p / 2];
+        x1[p] = (p & 1) ? bf16_hi(u1) : bf16_lo(u1);
+        x2[p] = (p & 1) ? bf16_hi(u2) : bf16_lo(u2);
+      }
     }
     float ss = 0.f;
 #pragma unroll
@@ -115,6 +149,9 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(Args a) {
       *(uint32_t*)(dst + o1) = pack_bf16(y1[0], y1[1]);
       *(uint32_t*)(dst + o2) = pack_bf16(y2[0], y2[1]);
     }
+    wc = wn;
+#pragma unroll
+    for (int p = 0; p < PPL; ++p) { g1[p] = n1[p]; g2[p] = n2[p]; }
   }
 }
 
