@@ -209,76 +209,89 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
   } else
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    float x[KC][8];
-    if (in_seq[rb]) {
-      const uint16_t* src = (const uint16_t*)a.q + bl * a.qs0 + (tok0 + row[rb]) * a.qs1 + head * a.qs2;
+    // Every load of the row block (the q row, its row of the rotary table and
+    // the gammas) is issued before any of them is used, so their latencies
+    // overlap; a row past the end reads the last row and is zeroed.
+    const int rowc = min(row[rb], S - 1);
+    const uint16_t* src = (const uint16_t*)a.q + bl * a.qs0 + (tok0 + rowc) * a.qs1 + head * a.qs2;
+    // (cos, sin) of this token's pairs from the table the prologue pass wrote
+    const float2* csrow = a.cs + ((int64_t)bl * Sx + tok0 + rowc) * (D / 2);
+    const float* gq = a.gq + head * a.gqs;
+    const float c2 = a.c2;
+    u32x4 qw[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qw[c] = *(const u32x4*)(src + c * 16 + hf * 8);
+    // the row as fp32 (zeros past the end) and its RMSNorm factor
+    auto unpack_rms = [&](float (&x)[KC][8]) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const u32x4 w = *(const u32x4*)(src + c * 16 + hf * 8);
+        const u32x4 w = in_seq[rb] ? qw[c] : z;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[c][2 * e] = bf16_lo(w[e]);
           x[c][2 * e + 1] = bf16_hi(w[e]);
         }
       }
-    } else {
+      float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < KC; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[c][e] = 0.f;
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
-    ss = half_swap_sum(ss);
-    const float r = rsqrtf(ss * (1.0f / D) + a.eps);
-    const float c2 = a.c2;
-    // (cos, sin) of this token's pairs from the table the prologue pass wrote
-    const float2* csrow = a.cs + ((int64_t)bl * Sx + tok0 + min(row[rb], S - 1)) * (D / 2);
-    const float* gq = a.gq + head * a.gqs;
+        for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
+      ss = half_swap_sum(ss);
+      return rsqrtf(ss * (1.0f / D) + a.eps);
+    };
     if (a.inter) {
       // pairs (2j, 2j + 1): elements e, e + 1 of one chunk, pair index
       // (c*16 + hf*8 + e) / 2; Q' keeps the element order of q
+      f32x4 ga[KC], gb[KC], t01[KC], t23[KC];
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        const f32x4 ga = *(const f32x4*)(gq + c * 16 + hf * 8);
-        const f32x4 gb = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
-        const f32x4 t01 = *(const f32x4*)(csrow + c * 8 + hf * 4);
-        const f32x4 t23 = *(const f32x4*)(csrow + c * 8 + hf * 4 + 2);
+        ga[c] = *(const f32x4*)(gq + c * 16 + hf * 8);
+        gb[c] = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
+        t01[c] = *(const f32x4*)(csrow + c * 8 + hf * 4);
+        t23[c] = *(const f32x4*)(csrow + c * 8 + hf * 4 + 2);
+      }
+      float x[KC][8];
+      const float r = unpack_rms(x);
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float g1 = e < 4 ? ga[e] : gb[e - 4];
-          const float g2 = e < 4 ? ga[e + 1] : gb[e - 3];
-          const f32x4 t = e < 4 ? t01 : t23;
+          const float g1 = e < 4 ? ga[c][e] : gb[c][e - 4];
+          const float g2 = e < 4 ? ga[c][e + 1] : gb[c][e - 3];
+          const f32x4 t = e < 4 ? t01[c] : t23[c];
           const float cs = t[(e & 2)], sn = t[(e & 2) + 1];
           const float u = x[c][e] * r * g1;
           const float w = x[c][e + 1] * r * g2;
           qf[rb][c][e] = (__bf16)((u * cs - w * sn) * c2);
           qf[rb][c][e + 1] = (__bf16)((w * cs + u * sn) * c2);
         }
+    } else {
+      f32x4 g1a[KC / 2], g1b[KC / 2], g2a[KC / 2], g2b[KC / 2], t4[KC / 2][4];
+#pragma unroll
+      for (int c = 0; c < KC / 2; ++c) {
+        g1a[c] = *(const f32x4*)(gq + c * 16 + hf * 8);
+        g1b[c] = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
+        g2a[c] = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8);
+        g2b[c] = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8 + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t4[c][e] = *(const f32x4*)(csrow + c * 16 + hf * 8 + 2 * e);
       }
-    } else
+      float x[KC][8];
+      const float r = unpack_rms(x);
 #pragma unroll
-    for (int c = 0; c < KC / 2; ++c) {
-      const f32x4 g1a = *(const f32x4*)(gq + c * 16 + hf * 8);
-      const f32x4 g1b = *(const f32x4*)(gq + c * 16 + hf * 8 + 4);
-      const f32x4 g2a = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8);
-      const f32x4 g2b = *(const f32x4*)(gq + D / 2 + c * 16 + hf * 8 + 4);
-      f32x4 t4[4];
+      for (int c = 0; c < KC / 2; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t4[e] = *(const f32x4*)(csrow + c * 16 + hf * 8 + 2 * e);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g1 = e < 4 ? g1a[e & 3] : g1b[e & 3];
-        const float g2 = e < 4 ? g2a[e & 3] : g2b[e & 3];
-        const float cs = t4[e >> 1][(e & 1) * 2], sn = t4[e >> 1][(e & 1) * 2 + 1];
-        const float u = x[c][e] * r * g1;
-        const float w = x[c + KC / 2][e] * r * g2;
-        qf[rb][c][e] = (__bf16)((u * cs - w * sn) * c2);
-        qf[rb][c + KC / 2][e] = (__bf16)((w * cs + u * sn) * c2);
-      }
+        for (int e = 0; e < 8; ++e) {
+          const float g1 = e < 4 ? g1a[c][e & 3] : g1b[c][e & 3];
+          const float g2 = e < 4 ? g2a[c][e & 3] : g2b[c][e & 3];
+          const float cs = t4[c][e >> 1][(e & 1) * 2], sn = t4[c][e >> 1][(e & 1) * 2 + 1];
+          const float u = x[c][e] * r * g1;
+          const float w = x[c + KC / 2][e] * r * g2;
+          qf[rb][c][e] = (__bf16)((u * cs - w * sn) * c2);
+          qf[rb][c + KC / 2][e] = (__bf16)((w * cs + u * sn) * c2);
+        }
     }
   }
 
