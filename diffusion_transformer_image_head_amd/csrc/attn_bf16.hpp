@@ -190,6 +190,13 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
     return;
   }
 
+  // gamma_k for the logit bound, loaded with the Q prologue's loads
+  float gk0 = 0.f, gk1 = 0.f;
+  if constexpr (!PRE) {
+    const float* gkp = a.gk + head * a.gqs;
+    gk0 = gkp[lane];
+    if constexpr (D > 64) gk1 = gkp[lane + 64];
+  }
   // ---- Q prologue: RMSNorm + M-RoPE in fp32, scaled by softmax_scale*log2(e),
   // one bf16 rounding, kept as the B operand of S^T: lane (m, hf) holds
   // Q'[row][c*16 + hf*8 + e].
@@ -497,9 +504,8 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
   // subnormal range, which the matrix cores flush).
   bool fixed_max = false;
   if constexpr (!PRE) {
-    const float* gk = a.gk + head * a.gqs;
-    float gmax = fabsf(gk[lane]);
-    if constexpr (D > 64) gmax = fmaxf(gmax, fabsf(gk[lane + 64]));
+    float gmax = fabsf(gk0);
+    if constexpr (D > 64) gmax = fmaxf(gmax, fabsf(gk1));
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, o, 64));
     const float kb = gmax * sqrtf((float)D) * (1.0f + 1.0f / 128);
