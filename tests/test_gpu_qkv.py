@@ -8,7 +8,7 @@ import pytest
 from diffusion_transformer_image_head_amd.workloads import make_qkv_workload
 from oracle.qkv import e4m3_decode, oracle_qkv_proj
 from oracle.reference import oracle_fwd
-from tests.gpu_util import check_parity, errors, say
+from tests.gpu_util import check_parity, say
 
 pytestmark = pytest.mark.gpu
 

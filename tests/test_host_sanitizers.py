@@ -11,7 +11,6 @@ against the calling contract.
 """
 
 import os
-import shutil
 import subprocess
 
 import pytest
