@@ -13,18 +13,24 @@ Timing protocol. Before the counted warm-up, a declared time-based pre-warm
 runs back-to-back steps for ``--prewarm-s`` seconds (the engine clock of a
 GPU that was idle ramps up over the first few hundred milliseconds of load;
 the pre-warm and its length are reported as ``prewarm``). Then ``--warmup``
-untimed steps, then exactly ``--steps`` timed steps, each bracketed by HIP
-events on the stream the kernels run on.
+untimed steps, then exactly ``--steps`` timed steps launched back to back on
+the stream the kernels run on, bracketed by synchronisation and by one HIP
+event at each end of the region: an event recorded between two kernels holds
+the next launch for a few microseconds, so none is recorded inside it.
 
 Prints one JSON line. ``value`` is algorithmic TFLOP/s of the whole timed
 region (4*H*D*sum_b n_b^2 over real tokens, times the steps, over the events
-around all of them); ``roofline`` is the attend stage's rate at its MEDIAN
-per-step event time against the bf16 dense MFMA peak, with min / p90 / max and
-the first- and last-quarter medians beside it; ``cpu_baseline`` is the fp64
-oracle timed on the host on the same workload (with the GPU output checked
-against it). ``extras`` carries the grouped guided step, the backward and the
-fp8 projection at the same shape, each timed after the headline region with
-its own warm-up (medians of per-call events).
+around all of them). ``roofline`` is the attend stage's rate at its mean time
+over ``--steps`` attend-stage calls launched back to back after the timed
+region, against the bf16 dense MFMA peak. Then ``--steps`` more steps with an
+event after every stage give the per-step distributions (``attend_ms``,
+``step_ms``: median, min / p90 / max, first- and last-quarter medians; these
+include the events' own gaps). ``cpu_baseline`` is the fp64 oracle timed on
+the host on the same workload (with the GPU output checked against it).
+``extras`` carries the grouped guided step, the backward and the fp8
+projection at the same shape, each timed after the headline region with its
+own warm-up, the same way (rates from back-to-back calls, per-call event
+medians beside them).
 """
 
 from __future__ import annotations
@@ -163,31 +169,47 @@ def prewarm(stages, seconds: float) -> dict:
     return {"seconds": round(time.perf_counter() - t0, 3), "calls": n}
 
 
+def back_to_back(stages, steps: int) -> tuple:
+    """`steps` calls launched back to back on the current stream, bracketed by
+    synchronisation and one HIP event at each end; no event inside (an event
+    recorded between two kernels holds the next launch for a few
+    microseconds). Returns (event ms of the region, wall seconds)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        for fn in stages:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), time.perf_counter() - wall0
+
+
 def timed_calls(stages, warmup: int, steps: int) -> dict:
-    """`warmup` untimed calls, then `steps` calls each bracketed by HIP events
-    on the current stream (the stream the binding launches on), with one more
-    event after every stage. Returns per-call totals and per-stage times (ms)
-    and the whole timed region's event time."""
+    """`warmup` untimed calls; the timed region: `steps` calls back to back
+    (back_to_back), whose event time gives the throughput; then `steps` more
+    calls, each bracketed by HIP events with one more event after every stage,
+    for per-call and per-stage distributions (these include the events' own
+    gaps). Returns the region's time, per-call totals and per-stage times
+    (ms)."""
     import torch
     for _ in range(warmup):
         for fn in stages:
             fn()
-    torch.cuda.synchronize()
+    region, wall = back_to_back(stages, steps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
-    end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
         for j, fn in enumerate(stages):
             fn()
             ev[i][j + 1].record()
-    end.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
     total = [e[0].elapsed_time(e[-1]) for e in ev]
     per_stage = [[e[j].elapsed_time(e[j + 1]) for e in ev] for j in range(len(stages))]
-    return {"total": total, "stages": per_stage, "region_ms": ev[0][0].elapsed_time(end), "wall_s": wall}
+    return {"total": total, "stages": per_stage, "region_ms": region, "wall_s": wall}
 
 
 def tflops(flops: float, ms: float) -> float:
@@ -377,16 +399,15 @@ def bench_cfg(args):
     sep = timed_calls([separate], args.warmup, args.steps)
     grp = timed_calls([grouped], args.warmup, args.steps)
     ms = grp["region_ms"] / args.steps
-    med = float(np.median(grp["total"]))
     rec = base_record(args, METRIC + " (guided step: cond + uncond)", tflops(flops, ms), ms,
                       "cfg1024: 1024px cond (B=1 H=32 D=128, 512 text + 64x64 image) "
                       "+ image-only uncond (4096 tokens), one grouped call")
-    rec["roofline"] = roofline(tflops(flops, med), "whole grouped call (prologues + attention + merge)",
-                               kernel_ms=round(med, 5))
+    rec["roofline"] = roofline(tflops(flops, ms), "whole grouped call (prologues + attention + merge)",
+                               kernel_ms=round(ms, 5), statistic="mean over the back-to-back timed calls (HIP events at the region's ends)")
     rec["prewarm"] = pw
     rec["call_ms"] = summarize(grp["total"])
-    rec["separate_calls"] = {"ms_median": round(float(np.median(sep["total"])), 5),
-                             "value": round(tflops(flops, float(np.median(sep["total"]))), 3)}
+    sms = sep["region_ms"] / args.steps
+    rec["separate_calls"] = {"ms_mean": round(sms, 5), "value": round(tflops(flops, sms), 3)}
     if not args.no_cpu_baseline:
         base, par = cpu_baseline(cond, out.float().cpu().numpy().astype(np.float64), 1)
         rec["cpu_baseline"] = dict(base, sample="the conditional pass only (" + base["sample"] + ")")
@@ -404,17 +425,17 @@ def bench_qkv(args):
     tp = timed_calls([proj], args.warmup, args.steps)
     ta = timed_calls([attend], args.warmup, args.steps)
     ms = tp["region_ms"] / args.steps
-    med = float(np.median(tp["total"]))
     rec = base_record(args, "fp8 QKV projection + norm/rotation epilogue TFLOP/s (bf16 matrix cores)",
                       tflops(flops, ms), ms,
                       f"{args.config} qkv: tokens={w.batch * w.seq} hidden={w.heads * w.head_dim} "
                       f"out={3 * w.heads * w.head_dim}")
     rec["data"] = "synthetic (seeded N(0,1) x, N(0,1/hidden) weight quantized to e4m3 per row)"
-    rec["roofline"] = roofline(tflops(flops, med), "rope_table_kernel + qkv_proj_kernel", kernel_ms=round(med, 5))
+    rec["roofline"] = roofline(tflops(flops, ms), "rope_table_kernel + qkv_proj_kernel", kernel_ms=round(ms, 5),
+                               statistic="mean over the back-to-back timed calls (HIP events at the region's ends)")
     rec["prewarm"] = pw
     rec["call_ms"] = summarize(tp["total"])
-    am = float(np.median(ta["total"]))
-    rec["attention_on_operands"] = {"ms_median": round(am, 5), "TFLOP/s": round(tflops(att_flops, am), 3)}
+    am = ta["region_ms"] / args.steps
+    rec["attention_on_operands"] = {"ms_mean": round(am, 5), "TFLOP/s": round(tflops(att_flops, am), 3)}
     rec["kernel_source_hash"] = kernel_source_hash("qkv")
     if args.config == "1024px":
         rec["profile"] = path_profile_status("qkv_proj_1024px_kernel_trace.txt", "qkv")
@@ -428,13 +449,12 @@ def bench_bwd(args):
     pw = prewarm([step], args.prewarm_s)
     tb = timed_calls([step], args.warmup, args.steps)
     ms = tb["region_ms"] / args.steps
-    med = float(np.median(tb["total"]))
     bb, s, h, d = w.shape
     rec = base_record(args, "fused QK-norm+M-RoPE attention backward TFLOP/s (2.5x forward FLOPs)",
                       tflops(flops, ms), ms, f"{args.config} backward: B={bb} H={h} head_dim={d} tokens={s}")
     rec["data"] = DATA.replace("q/k/v", "q/k/v/dO")
-    rec["roofline"] = roofline(tflops(flops, med), "whole backward call (prologues, delta, dk/dv/dq, dgamma)",
-                               kernel_ms=round(med, 5))
+    rec["roofline"] = roofline(tflops(flops, ms), "whole backward call (prologues, delta, dk/dv/dq, dgamma)",
+                               kernel_ms=round(ms, 5), statistic="mean over the back-to-back timed calls (HIP events at the region's ends)")
     rec["prewarm"] = pw
     rec["call_ms"] = summarize(tb["total"])
     rec["kernel_source_hash"] = kernel_source_hash("backward")
@@ -482,7 +502,6 @@ def bench_packed(args):
     pw = prewarm([step], args.prewarm_s)
     tm = timed_calls([step], args.warmup, args.steps)
     ms = tm["region_ms"] / args.steps
-    med = float(np.median(tm["total"]))
     mult = 2.5 if args.backward else 1.0
     what = "backward" if args.backward else "forward"
     rec = base_record(args, f"fused QK-norm+M-RoPE attention {what} TFLOP/s, packed sequences"
@@ -490,7 +509,8 @@ def bench_packed(args):
                       f"{args.config} packed {what}: {len(lens)} sequences, {w.q.shape[0]} tokens, "
                       f"H={c['heads']} head_dim={c['head_dim']}")
     rec["config"]["cu_seqlens"] = [int(x) for x in w.cu_seqlens]
-    rec["roofline"] = roofline(tflops(mult * w.flops(), med), f"whole packed {what} call", kernel_ms=round(med, 5))
+    rec["roofline"] = roofline(tflops(mult * w.flops(), ms), f"whole packed {what} call", kernel_ms=round(ms, 5),
+                               statistic="mean over the back-to-back timed calls (HIP events at the region's ends)")
     rec["prewarm"] = pw
     rec["call_ms"] = summarize(tm["total"])
     print(json.dumps(rec), flush=True)
@@ -498,36 +518,41 @@ def bench_packed(args):
 
 def extras(args) -> dict:
     """The grouped guided step, the backward and the fp8 projection at the
-    1024px shape, each after its own warm-up; medians of per-call events."""
+    1024px shape, each after its own warm-up; rates from the mean of
+    back-to-back calls, with the median of per-call events beside them."""
     import numpy as np
     import torch
     res = {}
     warm, steps = max(args.warmup, 10), max(args.steps, 20)
     _, flops, grouped, _, _ = setup_cfg()
     g = timed_calls([grouped], warm, steps)
-    gm = float(np.median(g["total"]))
-    res["cfg1024_grouped"] = {"ms_median": round(gm, 5), "TFLOP/s": round(tflops(flops, gm), 3),
+    gm = g["region_ms"] / steps
+    res["cfg1024_grouped"] = {"ms_mean": round(gm, 5), "TFLOP/s": round(tflops(flops, gm), 3),
+                              "ms_median_events": round(float(np.median(g["total"])), 5),
                               "what": "cond 4608 + image-only uncond 4096 tokens, H=32, one grouped call"}
     torch.cuda.empty_cache()
     _, flops, step = setup_bwd("1024px")
     b = timed_calls([step], warm, steps)
-    bm = float(np.median(b["total"]))
-    res["backward_1024px"] = {"ms_median": round(bm, 5), "TFLOP/s": round(tflops(flops, bm), 3),
+    bm = b["region_ms"] / steps
+    res["backward_1024px"] = {"ms_mean": round(bm, 5), "TFLOP/s": round(tflops(flops, bm), 3),
+                              "ms_median_events": round(float(np.median(b["total"])), 5),
                               "what": "dq, dk, dv, dgammas; FLOPs 2.5x the forward's",
                               "kernel_source_hash": kernel_source_hash("backward"),
                               "profile": path_profile_status("attn_bwd_1024px_kernel_trace.txt", "backward")}
     torch.cuda.empty_cache()
     _, flops, proj, _, _ = setup_qkv("1024px")
     p = timed_calls([proj], warm, steps)
-    pm = float(np.median(p["total"]))
-    res["qkv_proj_1024px"] = {"ms_median": round(pm, 5), "TFLOP/s": round(tflops(flops, pm), 3),
+    pm = p["region_ms"] / steps
+    res["qkv_proj_1024px"] = {"ms_mean": round(pm, 5), "TFLOP/s": round(tflops(flops, pm), 3),
+                              "ms_median_events": round(float(np.median(p["total"])), 5),
                               "what": "x [4608, 4096] bf16 x fp8 e4m3 W [12288, 4096] with row scales, "
                                       "norm/rotation epilogue",
                               "kernel_source_hash": kernel_source_hash("qkv"),
                               "profile": path_profile_status("qkv_proj_1024px_kernel_trace.txt", "qkv")}
     for r in res.values():
         r["frac"] = round(r["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
-    res["protocol"] = f"{warm} warm-up + {steps} timed calls each, after the headline region"
+    res["protocol"] = (f"{warm} warm-up + {steps} back-to-back timed calls each (TFLOP/s from their mean), "
+                       f"then {steps} calls with per-call events (ms_median_events), after the headline region")
     return res
 
 
@@ -542,10 +567,12 @@ def bench_forward(args):
     tm = timed_calls(stages, args.warmup, args.steps)
     flops = w.flops()
     ms_step = tm["region_ms"] / args.steps
+    # the attend stage alone, back to back: its mean launch time
+    att_region, _ = back_to_back([stages[1]], args.steps)
+    att_mean = att_region / args.steps
     att = tm["stages"][1]
-    att_med = float(np.median(att))
     value = tflops(flops, ms_step)
-    achieved = tflops(flops, att_med)
+    achieved = tflops(flops, att_mean)
     rec = base_record(args, METRIC, value, ms_step,
                       f"{args.config}: B={b} H={h} head_dim={d} tokens={s} "
                       f"(text_pad={w.text_pad} + {w.grid[0]}x{w.grid[1]} image)")
@@ -553,8 +580,12 @@ def bench_forward(args):
                           "kprologue": args.kprologue,
                           "text_lens": None if w.seq_lens is None else [int(x) for x in w.seq_lens]})
     rec["roofline"] = roofline(achieved, "attn_bf16_kernel + split_merge_kernel (attend stage)",
-                               traffic=traffic_from_profile(args.config), kernel_ms=round(att_med, 5),
-                               statistic="median of per-step HIP events around the attend stage")
+                               traffic=traffic_from_profile(args.config), kernel_ms=round(att_mean, 5),
+                               statistic=f"mean over {args.steps} back-to-back attend-stage calls (HIP events "
+                                         "at the region's ends), after the timed steps")
+    rec["timing"] = (f"value: {args.steps} steps back to back, HIP events at the region's ends only; roofline: "
+                     f"{args.steps} attend-stage calls back to back; attend_ms / step_ms: {args.steps} more steps "
+                     "with an event after every stage (they include the events' own gaps)")
     rec["attend_ms"] = summarize(att)
     rec["step_ms"] = summarize(tm["total"])
     rec["prologue_ms_median"] = round(float(np.median(tm["stages"][0])), 5)
