@@ -67,6 +67,8 @@ class QkvDesc(ctypes.Structure):
 
 KPRO_NONE = 3
 _KPRO["none"] = KPRO_NONE
+KPRO_GIVEN = 4
+_KPRO["given"] = KPRO_GIVEN
 
 
 class LaunchPlan(ctypes.Structure):
@@ -223,7 +225,7 @@ def _checked(q, k, v, pos, gamma_q, gamma_k, seq_lens, out, return_lse, *, text_
     """Shape/dtype/device checks; returns (desc, out, lse, seq_lens)."""
     import torch
 
-    given = kprologue in ("none", KPRO_NONE)
+    given = kprologue in ("none", KPRO_NONE, "given", KPRO_GIVEN)
     for name, t in (("q", q), ("k", k), ("v", v), ("pos", pos), ("gamma_q", gamma_q),
                     ("gamma_k", gamma_k)):
         if t is None and given and name in ("pos", "gamma_q", "gamma_k"):

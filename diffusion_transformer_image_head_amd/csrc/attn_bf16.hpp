@@ -202,7 +202,11 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
   // Q'[row][c*16 + hf*8 + e].
   bf16x8 qf[RB][KC];
   if constexpr (PRE) {
-    // the operand as given: rows past the end read as zeros
+    // the operand as given (Q''), or a plain Q' times qmul =
+    // softmax_scale*log2(e) rounded again to bf16; rows past the end read as
+    // zeros
+    const float qmul = a.qmul;
+    const bool scale_q = qmul != 1.0f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const uint16_t* src = (const uint16_t*)a.q + bl * a.qs0 + (tok0 + min(row[rb], S - 1)) * a.qs1 + head * a.qs2;
@@ -210,7 +214,15 @@ __global__ __launch_bounds__(WAVES * 64, WAVES * RB >= 8 ? 1 : 2) void attn_bf16
       for (int c = 0; c < KC; ++c) {
         const u32x4 w = *(const u32x4*)(src + c * 16 + hf * 8);
         const u32x4 z = {0u, 0u, 0u, 0u};
-        qf[rb][c] = __builtin_bit_cast(bf16x8, in_seq[rb] ? w : z);
+        const u32x4 x = in_seq[rb] ? w : z;
+        qf[rb][c] = __builtin_bit_cast(bf16x8, x);
+        if (scale_q) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qf[rb][c][2 * e] = (__bf16)(bf16_lo(x[e]) * qmul);
+            qf[rb][c][2 * e + 1] = (__bf16)(bf16_hi(x[e]) * qmul);
+          }
+        }
       }
     }
   } else

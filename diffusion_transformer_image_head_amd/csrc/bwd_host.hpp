@@ -37,7 +37,7 @@ static int bwd_check(const mra_desc* d) {
   int rc = check_desc(d);
   if (rc != MRA_OK) return rc;
   if (d->dtype != MRA_BF16 || d->head_dim != 128) return MRA_ERR_UNSUPPORTED;
-  if (d->kprologue == MRA_KPRO_NONE) return MRA_ERR_UNSUPPORTED;
+  if (d->kprologue == MRA_KPRO_NONE || d->kprologue == MRA_KPRO_GIVEN) return MRA_ERR_UNSUPPORTED;
   return MRA_OK;
 }
 

@@ -52,6 +52,7 @@ struct Args {
   float c2;                 // softmax scale * log2(e)
   float scale;
   float pscale;             // factor applied by k_prologue_kernel before rounding
+  float qmul;               // given operands: factor q is multiplied by as it is loaded
   int32_t gqs;              // elements between the gamma rows of two heads (0: shared)
   int32_t inter;            // rotary pairs (2j, 2j + 1) instead of (j, j + D/2)
   Rope rope;

@@ -81,7 +81,9 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int resolve_kprologue(const mra_desc* d) {
-  return d->kprologue == MRA_KPRO_AUTO ? MRA_KPRO_PREPASS : d->kprologue;
+  const int k = d->kprologue == MRA_KPRO_AUTO ? MRA_KPRO_PREPASS : d->kprologue;
+  // plain given operands take the same kernels as scaled ones (q scaled on load)
+  return k == MRA_KPRO_GIVEN ? MRA_KPRO_NONE : k;
 }
 
 // Descriptor-only checks (no pointers).
@@ -100,7 +102,7 @@ int check_desc(const mra_desc* d) {
   if (!(d->eps >= 0.f) || !std::isfinite(d->eps)) return MRA_ERR_PARAM;
   if (!std::isfinite(d->softmax_scale)) return MRA_ERR_PARAM;
   if (d->dtype == MRA_BF16 && d->kprologue != MRA_KPRO_AUTO && d->kprologue != MRA_KPRO_FUSED &&
-      d->kprologue != MRA_KPRO_PREPASS && d->kprologue != MRA_KPRO_NONE)
+      d->kprologue != MRA_KPRO_PREPASS && d->kprologue != MRA_KPRO_NONE && d->kprologue != MRA_KPRO_GIVEN)
     return MRA_ERR_PARAM;
   if (d->rope_pairs != MRA_ROPE_HALF && d->rope_pairs != MRA_ROPE_INTERLEAVED) return MRA_ERR_PARAM;
   if (d->gamma_per_head != 0 && d->gamma_per_head != 1) return MRA_ERR_PARAM;
@@ -239,6 +241,7 @@ void fill_args(Args& a, const mra_desc* d, const void* q, const void* k, const v
   a.scale = d->softmax_scale > 0.f ? d->softmax_scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   a.c2 = (float)((double)a.scale * 1.4426950408889634);
   a.pscale = 1.0f;
+  a.qmul = d->kprologue == MRA_KPRO_GIVEN ? a.c2 : 1.0f;
   a.gqs = d->gamma_per_head ? d->head_dim : 0;
   a.inter = d->rope_pairs == MRA_ROPE_INTERLEAVED;
   const int half = d->head_dim / 2;
@@ -351,7 +354,7 @@ const char* mrope_attn_status_string(int status) {
     case MRA_ERR_UNSUPPORTED: return "unsupported configuration";
     case MRA_ERR_WORKSPACE: return "workspace missing or too small";
     case MRA_ERR_HIP: return "HIP launch or runtime error";
-    case MRA_ERR_PARAM: return "invalid theta/eps/softmax_scale/kprologue";
+    case MRA_ERR_PARAM: return "invalid theta/eps/softmax_scale/kprologue/rope_pairs/gamma_per_head, or group size";
     case MRA_ERR_SCRATCH: return "problem needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
@@ -364,8 +367,8 @@ int mrope_attn_validate(const mra_desc* d, const void* q, const void* k, const v
   int rc = check_desc(d);
   if (rc != MRA_OK) return rc;
   if (d->batch == 0 || d->seq == 0) return MRA_OK;
-  // operands given (MRA_KPRO_NONE): positions and gammas are not read
-  const bool given = d->dtype == MRA_BF16 && d->kprologue == MRA_KPRO_NONE;
+  // operands given (MRA_KPRO_NONE, MRA_KPRO_GIVEN): positions and gammas are not read
+  const bool given = d->dtype == MRA_BF16 && resolve_kprologue(d) == MRA_KPRO_NONE;
   if (!q || !k || !v || !out || (!given && (!pos || !gq || !gk))) return MRA_ERR_NULL;
   if ((rc = check_strides(d->q_stride, d->dtype)) != MRA_OK) return rc;
   if ((rc = check_strides(d->k_stride, d->dtype)) != MRA_OK) return rc;

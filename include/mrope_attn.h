@@ -73,7 +73,8 @@ typedef enum {
   MRA_ERR_UNSUPPORTED = -6, /* valid request this build does not implement */
   MRA_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
   MRA_ERR_HIP = -8,         /* a HIP launch or runtime call failed */
-  MRA_ERR_PARAM = -9,       /* theta/eps/scale/kprologue/rope_pairs/gamma_per_head invalid */
+  MRA_ERR_PARAM = -9,       /* theta/eps/scale/kprologue/rope_pairs/gamma_per_head invalid,
+                               or a group size outside 1..MRA_MAX_GROUP */
   MRA_ERR_SCRATCH = -10     /* mrope_attn_fwd_noalloc: the problem needs more scratch than
                                MRA_NOALLOC_SCRATCH_BYTES */
 } mra_status;
@@ -85,10 +86,16 @@ typedef enum {
   MRA_KPRO_AUTO = 0,    /* library's choice (currently MRA_KPRO_PREPASS) */
   MRA_KPRO_FUSED = 1,   /* applied while each K tile is staged into LDS */
   MRA_KPRO_PREPASS = 2, /* one pass writes K' (bf16) to the workspace first */
-  MRA_KPRO_NONE = 3     /* q and k already hold the operands Q'' and K' (as written
-                           by mrope_qkv_proj with the same softmax_scale): no norm
-                           or rotation is applied; pos_thw, gamma_q, gamma_k are
-                           not read and may be NULL */
+  MRA_KPRO_NONE = 3,    /* q and k already hold the operands Q'' and K' (as written
+                           by mrope_qkv_proj with the same softmax_scale): q is
+                           Q' already multiplied by softmax_scale * log2(e); no
+                           norm or rotation is applied; pos_thw, gamma_q, gamma_k
+                           are not read and may be NULL */
+  MRA_KPRO_GIVEN = 4    /* q and k hold Q' and K', normalised and rotated but not
+                           scaled: q is multiplied by softmax_scale * log2(e) as
+                           it is loaded (one more bf16 rounding than
+                           MRA_KPRO_NONE); no norm or rotation is applied;
+                           pos_thw, gamma_q, gamma_k are not read and may be NULL */
 } mra_kprologue;
 
 /* Which elements of a head row form rotary pair j. The pages do not say;

@@ -91,7 +91,8 @@ void walk(const mra_desc& d) {
   const int rb = mrope_attn_bwd(&d, P(), P(), P(), (const int32_t*)P(), (const float*)P(), (const float*)P(),
                                 nullptr, P(), (const float*)P(), P(), P(), P(), P(), (float*)P(), (float*)P(),
                                 bneed ? P() : nullptr, bneed, nullptr);
-  if (v == MRA_OK && !empty && d.dtype == MRA_BF16 && d.head_dim == 128 && d.kprologue != MRA_KPRO_NONE)
+  if (v == MRA_OK && !empty && d.dtype == MRA_BF16 && d.head_dim == 128 && d.kprologue != MRA_KPRO_NONE &&
+      d.kprologue != MRA_KPRO_GIVEN)
     EXPECT(rb == MRA_ERR_HIP && bneed > 0, rb);
   else
     EXPECT(rb != MRA_ERR_HIP || v != MRA_OK, rb);
@@ -157,7 +158,7 @@ int main() {
                            {0, 100, 2, 128, 0},     {2, 0, 2, 128, 0},        {1, 261632, 32, 128, 512}};
   for (const auto& s : shapes) {
     for (int dt = 0; dt < 2; ++dt)
-      for (int kp = 0; kp < 4; ++kp) {
+      for (int kp = 0; kp < 6; ++kp) {  // every mode, then one unknown
         mra_desc d = make(s[0], s[1], s[2], s[3], s[4], dt);
         d.kprologue = kp;
         walk(d);
@@ -169,7 +170,7 @@ int main() {
     const int hd = (rnd() % 8 == 0) ? 96 : ((rnd() & 1) ? 64 : 128);
     const int s = pick(0, (rnd() % 4 == 0) ? 40000 : 3000);
     mra_desc d = make(pick(0, 6), s, pick(1, 80), hd, s ? pick(0, s) : 0, (rnd() % 10 == 0) ? 2 : (int)(rnd() & 1));
-    d.kprologue = pick(0, 4);
+    d.kprologue = pick(0, 5);
     d.rope_pairs = (rnd() % 20 == 0) ? 2 : (int)(rnd() & 1);
     d.gamma_per_head = (rnd() % 20 == 0) ? 3 : (int)(rnd() & 1);
     if (rnd() % 10 == 0) d.section[0] += 1;

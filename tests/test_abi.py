@@ -523,6 +523,18 @@ def test_kprologue_none_needs_no_positions_or_table(lib):
     assert _bwd(desc(kprologue="none")) == -6
 
 
+def test_kprologue_given_plain_operands(lib):
+    # plain Q', K' (q scaled as it is loaded): the same contract as Q'', K'
+    d = desc(kprologue="given")
+    assert d.kprologue == 4
+    assert val(d, pos=None, gq=None, gk=None) == 0
+    for kw in (dict(), dict(batch=1, seq=4608, heads=32, text_pad=512)):
+        assert B.workspace_size(desc(kprologue="given", **kw)) == B.workspace_size(desc(kprologue="none", **kw))
+    assert _bwd(desc(kprologue="given")) == -6
+    assert val(desc(kprologue=5)) == -9                         # unknown mode
+    assert "rope_pairs" in B.status_string(-9)
+
+
 def _qkv(d, **ptr):
     p = dict(x=FAKE, w=FAKE, s=FAKE, pos=FAKE, gq=FAKE, gk=FAKE, q=FAKE, k=FAKE, v=FAKE, ws=FAKE,
              n=1 << 40)
