@@ -336,7 +336,7 @@ hipError_t launch_fp32(Args& a, hipStream_t s, int qlen) {
 
 extern "C" {
 
-int mrope_attn_abi_version(void) { return 108; }
+int mrope_attn_abi_version(void) { return 109; }
 
 int mrope_attn_last_hip_error(const char** name) {
   if (name) *name = t_last_hip_error ? hipGetErrorName((hipError_t)t_last_hip_error) : "none";

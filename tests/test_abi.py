@@ -97,7 +97,7 @@ def test_struct_layouts_match_header(tmp_path, cls, struct):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mrope_attn_abi_version() == 108
+    assert lib.mrope_attn_abi_version() == 109
     for st in range(0, -11, -1):
         s = B.status_string(st)
         assert s and s != "unknown status"
