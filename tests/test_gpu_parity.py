@@ -377,7 +377,25 @@ def test_tail_split_full(shape):
     _full_check(w)
 
 
-@pytest.mark.parametrize("name", ["h36", "2048px", "conv"])
+def test_config_h36_full():
+    """36 heads at 1024px (8-wave workgroups, 648 tiles of 256 rows, a
+    136-tile last wave not cut): every output and LSE against the oracle."""
+    say("case: h36 config, all outputs")
+    _full_check(config_workload("h36"))
+
+
+def test_config_conv_full():
+    """The ragged 1024px batch of two under the other conventions (a gamma
+    per head, interleaved rotary pairs): every output and LSE against the
+    oracle, and exact zeros on the padded query rows."""
+    say("case: conv config, all outputs")
+    w = config_workload("conv")
+    out, _ = _full_check(w)
+    for b, l in enumerate(w.seq_lens):
+        assert np.all(out[b, int(l):w.text_pad] == 0)
+
+
+@pytest.mark.parametrize("name", ["2048px"])
 def test_config_sampled_rows(name):
     say(f"case: {name} config, sampled rows")
     w = config_workload(name)
