@@ -31,6 +31,13 @@ the host on the same workload (with the GPU output checked against it).
 projection at the same shape, each timed after the headline region with its
 own warm-up, the same way (rates from back-to-back calls, per-call event
 medians beside them).
+
+Runtime setting. Unless the environment already sets it, the process asks the
+HIP runtime to keep kernel arguments in device memory
+(``HIP_FORCE_DEV_KERNARG=1``, read when the runtime initialises, so it is set
+before torch is imported). Back-to-back launches then start about 3 us
+sooner; the kernels and their results are the same either way. The setting
+in force is reported as ``runtime_env``.
 """
 
 from __future__ import annotations
@@ -44,6 +51,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+os.environ.setdefault("HIP_FORCE_DEV_KERNARG", "1")
 
 METRIC = "fused QK-norm+M-RoPE attention TFLOP/s & % bf16 MFMA peak, 4608 tok"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
@@ -382,7 +390,8 @@ def base_record(args, metric, value, ms, workload, dtype="bf16"):
     return {"metric": metric, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-            "data": DATA, "config": {"workload": workload}}
+            "data": DATA, "config": {"workload": workload},
+            "runtime_env": {"HIP_FORCE_DEV_KERNARG": os.environ.get("HIP_FORCE_DEV_KERNARG")}}
 
 
 def roofline(achieved, kernel, **kw):
